@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Attention-forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one ``attn_fwd`` call (the whole hot path: Q-tile load, K/V tile
+stream, scores, mask, online softmax, P.V, epilogue) over the workload's
+synthetic inputs, which are generated on the host from a fixed seed and are
+resident in HBM before timing starts.  The default workload is causal
+prefill B=1, H=32, S=4096, d=128 in bf16 with fp32 accumulation.
+
+Prints one JSON line with the throughput in TFLOP/s (4*B*H*Sq*Skv*d, halved
+for causal), a ``roofline`` object for the attention kernel (MFMA-bound;
+achieved TFLOP/s from HIP events around each launch on the launch stream,
+against the MI355X dense bf16 MFMA peak) and a ``cpu_baseline`` object (the
+fp64 oracle timed on a bounded sample of the same workload on the host).
+
+``--copy-probe BYTES`` instead times a plain device-to-device copy of BYTES
+bytes; its rocprofv3 FETCH_SIZE / WRITE_SIZE readings calibrate the HBM
+counters against a transfer of known size.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % MFMA peak (bf16 H=32 S=4096 d=128 causal)"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_h32_s4096_d128.json")
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_device.h", "attn_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tiled_online_softmax_05_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were
+    taken on the current kernel source (else None)."""
+    if workload != "prefill_h32_s4096_d128" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(q, k, v, causal: bool, budget_s: float) -> dict:
+    """The fp64 oracle, as it stands, on whole heads of the same inputs,
+    for about ``budget_s`` seconds; scaled to TFLOP/s with the same FLOP
+    formula as the GPU figure."""
+    import oracle
+    from seeded_inputs import to_f64
+    from tiled_online_softmax_05_amd.accounting import attention_flops
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    _, H, Sq, d = q.shape
+    Skv = k.shape[2]
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    while done < H:
+        qh, kh, vh = to_f64(q[0, done]), to_f64(k[0, done]), to_f64(v[0, done])
+        oracle.direct_attention(qh, kh, vh, scale=1.0 / math.sqrt(d), causal=causal)
+        flops += attention_flops(1, 1, Sq, Skv, d, causal)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {H} heads (B=1, S={Sq}, d={d}, causal={causal}), fp64 numpy "
+                      f"direct attention, {dt:.1f} s"}
+
+
+def copy_probe(nbytes: int, steps: int) -> None:
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "steps": steps}), flush=True)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_h32_s4096_d128")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for cpu_baseline (0 disables it)")
+    ap.add_argument("--tiles", default=None, help="force BMxBN, e.g. 128x64")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if a.copy_probe:
+        copy_probe(a.copy_probe, max(1, a.steps))
+        return 0
+
+    from seeded_inputs import WORKLOADS, make_tensors
+    from tiled_online_softmax_05_amd import binding
+    from tiled_online_softmax_05_amd.accounting import attention_flops, compulsory_bytes
+
+    w = WORKLOADS[a.workload]
+    causal = True in w.causal_modes
+    dev = torch.device("cuda", 0)
+    q_h, k_h, v_h = make_tensors(w)
+    q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
+    tiles = tuple(int(x) for x in a.tiles.split("x")) if a.tiles else w.tiles
+    odt = q.dtype
+    out = torch.empty(q.shape, dtype=odt, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    code = binding.F32 if odt == torch.float32 else binding.BF16
+    dtype_name = "f32" if odt == torch.float32 else "bf16"
+    scale = 1.0 / math.sqrt(w.d)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    if tiles is None:
+        tiles_used = binding.select_tiles(w.d, w.Sq, w.Skv, w.B * w.H, code, causal)[:2]
+    else:
+        tiles_used = tiles
+
+    def step():
+        binding.fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        w.B, w.H, w.Sq, w.Skv, w.d, scale, causal, code, sp, tiles)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` launches, HIP events around each on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(launch_ms) / len(launch_ms)
+    med_ms = sorted(launch_ms)[len(launch_ms) // 2]
+
+    flops = attention_flops(w.B, w.H, w.Sq, w.Skv, w.d, causal)
+    ms_per_step = wall * 1e3 / a.steps
+    value = flops / (wall / a.steps) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype_name]
+    in_b = 4 if dtype_name == "f32" else 2
+    comp = compulsory_bytes(w.B, w.H, w.Sq, w.Skv, w.d, in_b, in_b)
+    traffic = measured_traffic(a.workload)
+
+    rec = {
+        "metric": METRIC if a.workload == "prefill_h32_s4096_d128" else f"attention fwd TFLOP/s ({a.workload})",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+        "config": {"workload": a.workload, "B": w.B, "H": w.H, "Sq": w.Sq, "Skv": w.Skv,
+                   "d": w.d, "causal": causal, "tiles": list(tiles_used),
+                   "input_dist": w.dist, "seed": w.seed},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "launch_ms_avg": round(avg_ms, 5), "launch_ms_median": round(med_ms, 5),
+                     "flops_per_launch": flops, "compulsory_bytes_per_launch": comp,
+                     "compulsory_GBps": round(comp / (avg_ms * 1e-3) / 1e9, 1),
+                     "hbm_peak_GBps": PEAK_HBM_GBS},
+    }
+    if a.cpu_budget > 0:
+        rec["cpu_baseline"] = cpu_baseline(q_h, k_h, v_h, causal, a.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,128 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) tiled online-softmax attention
+ * forward library (libattn.so).
+ *
+ * The operation is exact scaled-dot-product attention,
+ *
+ *     O_i   = sum_{j in Vis(i)} exp(s_ij - m_i) v_j / l_i,
+ *     s_ij  = scale * q_i . k_j,   m_i = max_j s_ij,   l_i = sum_j exp(s_ij - m_i),
+ *     LSE_i = m_i + ln l_i,
+ *
+ * as defined by the direct reference of "Verify tiled attention" (section
+ * "Compare the attention outputs") and by "FlashAttention implemented,
+ * verified and measured" (section "The reference implementation, in full").
+ * The library computes it tile by tile with the online softmax of "Tiled
+ * attention: preserving results without a full score matrix" (section
+ * "Online normalization"): per query row a running maximum m, a normaliser l
+ * and an unnormalised accumulator a, with l and a rescaled by exp(m_old -
+ * m_new) whenever a key/value tile raises the maximum, and O = a / l at the
+ * end.  The score matrix never leaves the chip.
+ *
+ * Visibility: key j is visible to query row i iff j < Skv and, for causal
+ * attention, j <= i + (Skv - Sq) (the "j <= i" causal rule of the lab page,
+ * aligned to the end of the key sequence when Sq != Skv).  A row with no
+ * visible key (Skv == 0, or causal with i < Sq - Skv) gets O = 0 and
+ * LSE = -inf; no NaN is produced.
+ *
+ * Layout (all tensors dense, row-major, the head dimension fastest):
+ *     q, o : [B, H, Sq,  d]
+ *     k, v : [B, H, Skv, d]       (value width equals d)
+ *     lse  : [B, H, Sq]  float32  (natural log of the sum of exponentials
+ *                                  of the scaled scores)
+ *
+ * Ownership and execution: every pointer is a device pointer on the current
+ * HIP device, owned by the caller.  The library allocates no device memory,
+ * never synchronises, and only enqueues work on `stream` (a hipStream_t; NULL
+ * means the null stream).  Calls return as soon as the work is enqueued;
+ * faults inside the kernels surface at the caller's next synchronisation.
+ * Argument validation happens on the host before any HIP call.  All entry
+ * points are thread-safe; the error message is kept per thread.  For a fixed
+ * tile configuration results are bitwise deterministic (no atomics).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  Accumulation is always at least fp32. */
+typedef enum {
+    ATTN_F32 = 0,          /* q, k, v, o float32.  Scores are accumulated in
+                              float64 (fp32 x fp32 products are exact there) so
+                              that scores of magnitude ~1e2-1e3 keep their
+                              fp32-level relative accuracy after the max shift;
+                              exponentials, l and P.V are fp32.              */
+    ATTN_BF16 = 1,         /* q, k, v, o bfloat16; QK^T and P.V on bf16 MFMA
+                              with fp32 accumulation, P rounded to bf16 (RNE). */
+    ATTN_BF16_OUT_F32 = 2  /* q, k, v bfloat16, o float32 (same arithmetic as
+                              ATTN_BF16, output not rounded to bf16).         */
+} attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,  /* null pointer for a non-empty tensor, negative
+                                  size, non-finite or non-positive scale,
+                                  unknown dtype, causal not 0/1, size overflow,
+                                  o aliasing an input                         */
+    ATTN_ERR_UNSUPPORTED = 2,  /* head dim or forced tile shape not built      */
+    ATTN_ERR_MISALIGNED = 3,   /* a pointer not 16-byte aligned                */
+    ATTN_ERR_HIP = 4           /* the HIP runtime reported an error at launch  */
+} attn_status;
+
+/*
+ * attn_fwd -- enqueue O (and LSE) = attention(q, k, v) on `stream`.
+ *
+ *   q, k, v  : inputs, layout above, element type per `dtype`.
+ *   o        : output [B, H, Sq, d]; must not overlap q, k, v or lse.
+ *   lse      : output [B, H, Sq] float32, or NULL to skip it.
+ *   B, H     : batch and heads (>= 0).
+ *   Sq, Skv  : query and key lengths (>= 0).  Sq == 0 is a no-op.
+ *   d        : head dimension: 32, 64 or 128 (fp32); 64 or 128 (bf16).
+ *   scale    : score scale, finite and > 0 (usually 1/sqrt(d)).
+ *   causal   : 0 or 1 (end-aligned mask above).
+ *   dtype    : an attn_dtype.
+ *   stream   : hipStream_t or NULL.
+ * Returns an attn_status; on failure attn_last_error() describes it and
+ * nothing was enqueued (except for ATTN_ERR_HIP, reported after a launch).
+ * Tiles come from attn_select_tiles().
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Sq, int Skv, int d, float scale, int causal,
+             int dtype, void* stream);
+
+/*
+ * attn_fwd_tiles -- attn_fwd with a forced tile shape: `block_m` query rows
+ * and `block_n` key rows per tile (the block_q / block_kv of the tiled lab
+ * function on "Verify tiled attention").  block_m = block_n = 0 means "use
+ * the selector".  Built shapes:
+ *   ATTN_F32            block_m in {16, 32, 64},  block_n in {16, 32, 64}
+ *   ATTN_BF16[_OUT_F32] block_m in {64, 128},     block_n in {32, 64}
+ * Any other pair returns ATTN_ERR_UNSUPPORTED.
+ */
+int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Skv, int d, float scale, int causal,
+                   int dtype, void* stream, int block_m, int block_n);
+
+/*
+ * attn_select_tiles -- the tile / occupancy selector (host only, no HIP
+ * call).  Writes the tile shape attn_fwd would use for this problem:
+ * query rows per workgroup, key rows per tile, 64-wide waves per workgroup
+ * and LDS bytes per workgroup.  `BH` is B * H.  Any output pointer may be
+ * NULL.  Returns ATTN_OK, ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED.
+ */
+int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal,
+                      int* block_m, int* block_n, int* waves, int* lds_bytes);
+
+/* attn_last_error -- message for the last non-OK status on this thread
+ * ("" if none).  The string stays valid until the next call on the thread. */
+const char* attn_last_error(void);
+
+/* attn_version -- library ABI version (major * 100 + minor). */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

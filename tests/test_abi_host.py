@@ -1,0 +1,126 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the selector is a pure host function, and every invalid
+argument is rejected on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tiled_online_softmax_05_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        pytest.fail("libattn.so is not built; run python -m tiled_online_softmax_05_amd.build")
+    return B.load()
+
+
+def test_header_declares_the_binding_surface():
+    assert _declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version(lib):
+    assert lib.attn_version() == 100
+
+
+@pytest.mark.parametrize("args,want", [
+    # (d, Sq, Skv, BH, dtype, causal) -> (block_m, block_n, waves)
+    ((32, 64, 64, 1, B.F32, 1), (16, 64, 1)),
+    ((64, 512, 512, 8, B.F32, 0), (16, 64, 1)),
+    ((32, 8, 1000, 6, B.F32, 1), (16, 64, 1)),
+    ((32, 8, 16, 6, B.F32, 0), (16, 16, 1)),
+    ((128, 4096, 4096, 32, B.BF16, 1), (128, 64, 4)),
+    ((128, 32768, 32768, 64, B.BF16, 1), (128, 64, 4)),
+    ((128, 256, 256, 2, B.BF16, 1), (64, 64, 2)),
+    ((64, 4096, 4096, 32, B.BF16_OUT_F32, 0), (128, 64, 4)),
+])
+def test_selector(lib, args, want):
+    bm, bn, waves, lds = B.select_tiles(*args)
+    assert (bm, bn, waves) == want
+    assert 0 < lds <= 160 * 1024
+
+
+def test_selector_rejects(lib):
+    with pytest.raises(B.AttnError) as e:
+        B.select_tiles(48, 64, 64, 1, B.F32, 0)
+    assert e.value.status == B.ERR_UNSUPPORTED
+    with pytest.raises(B.AttnError) as e:
+        B.select_tiles(128, 64, 64, 1, 7, 0)
+    assert e.value.status == B.ERR_INVALID_ARG
+
+
+# Fake device addresses: every call below fails validation, so nothing is
+# ever dereferenced and no HIP call is made.
+A0, A1, A2, A3, A4 = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
+
+
+def _call(lib, q=A0, k=A1, v=A2, o=A3, lse=A4, Bn=1, H=2, Sq=64, Skv=64, d=64, scale=0.125,
+          causal=0, dtype=B.F32, tiles=None):
+    args = (q, k, v, o, lse, Bn, H, Sq, Skv, d, scale, causal, dtype, None)
+    if tiles is None:
+        return lib.attn_fwd(*args)
+    return lib.attn_fwd_tiles(*args, *tiles)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.ERR_INVALID_ARG),
+    (dict(o=None), B.ERR_INVALID_ARG),
+    (dict(k=None), B.ERR_INVALID_ARG),
+    (dict(v=None), B.ERR_INVALID_ARG),
+    (dict(Bn=-1), B.ERR_INVALID_ARG),
+    (dict(Sq=-3), B.ERR_INVALID_ARG),
+    (dict(Skv=-1), B.ERR_INVALID_ARG),
+    (dict(d=0), B.ERR_INVALID_ARG),
+    (dict(d=48), B.ERR_UNSUPPORTED),
+    (dict(d=32, dtype=B.BF16), B.ERR_UNSUPPORTED),
+    (dict(dtype=3), B.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), B.ERR_INVALID_ARG),
+    (dict(scale=0.0), B.ERR_INVALID_ARG),
+    (dict(scale=-0.5), B.ERR_INVALID_ARG),
+    (dict(causal=2), B.ERR_INVALID_ARG),
+    (dict(q=A0 + 4), B.ERR_MISALIGNED),
+    (dict(o=A3 + 8), B.ERR_MISALIGNED),
+    (dict(lse=A4 + 2), B.ERR_MISALIGNED),
+    (dict(o=A0), B.ERR_INVALID_ARG),                     # o aliases q
+    (dict(o=A2 + 64), B.ERR_INVALID_ARG),                # o overlaps v
+    (dict(Bn=65536, H=65536), B.ERR_INVALID_ARG),        # B*H overflows
+    (dict(tiles=(48, 16)), B.ERR_UNSUPPORTED),
+    (dict(tiles=(16, 0)), B.ERR_INVALID_ARG),
+    (dict(tiles=(-16, 16)), B.ERR_INVALID_ARG),
+    (dict(dtype=B.BF16, tiles=(32, 64)), B.ERR_UNSUPPORTED),
+])
+def test_invalid_arguments_rejected_on_host(lib, kw, status):
+    assert _call(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_empty_problems_are_no_ops(lib):
+    # nothing to compute: OK without touching the (null) pointers or the GPU
+    assert _call(lib, q=None, k=None, v=None, o=None, lse=None, Sq=0) == B.OK
+    assert _call(lib, q=None, k=None, v=None, o=None, lse=None, Bn=0) == B.OK
+    assert lib.attn_last_error().decode() == ""
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(ValueError):
+        B.fwd(q, q, q)

@@ -1,0 +1,42 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// MFMA wrappers and the workgroup -> (head, query tile) order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Workgroup order.  Workgroups are numbered so that consecutive ids walk
+// over the (batch, head) pairs of one query-tile rank.  With causal masking
+// the rank runs from the last query tile (the most key tiles) to the first,
+// so the hardware dispatcher, which hands out workgroups in id order, starts
+// the longest ones first.  Because the dispatcher deals consecutive ids to
+// the 8 XCDs in turn, every query tile of head bh lands on XCD (bh mod 8)
+// whenever the number of heads is a multiple of 8, and that XCD's L2 keeps
+// the head's K/V tiles for all of them.
+__device__ __forceinline__ void tile_coords(int n_bh, int n_qt, bool causal, int& bh, int& qt) {
+    const int idx = blockIdx.x;
+    const int rank = idx / n_bh;
+    bh = idx - rank * n_bh;
+    qt = causal ? (n_qt - 1 - rank) : rank;
+}
+
+// Key range [0, kv_end) a workgroup of query rows [q_first, q_last] visits:
+// causal rows see keys j <= i + (Skv - Sq).
+__device__ __forceinline__ int kv_limit(int q_last, int Sq, int Skv, bool causal) {
+    if (!causal) return Skv;
+    int e = q_last + (Skv - Sq) + 1;
+    return e < 0 ? 0 : (e > Skv ? Skv : e);
+}
+
+}  // namespace attn

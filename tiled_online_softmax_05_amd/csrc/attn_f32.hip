@@ -1,0 +1,249 @@
+// fp32 attention forward for gfx950.
+//
+// The online softmax of "Tiled attention: preserving results without a full
+// score matrix" (section "Online normalization"), tiled over query rows and
+// key rows as in the tiled lab function of "Verify tiled attention".  Each
+// 64-wide wave owns 16 query rows; the workgroup's waves share one K/V tile
+// staged in LDS.
+//
+// Precision: scores are contracted on the fp64 matrix cores
+// (v_mfma_f64_16x16x4_f64).  Products of two fp32 numbers are exact in fp64,
+// so s_ij keeps full fp32-relative accuracy even when |s| reaches hundreds;
+// the max shift s - m is taken in fp64, then exponentials, the normaliser l
+// and the P.V contraction (v_mfma_f32_16x16x4_f32) run in fp32.
+//
+// Lane layout of a wave (lane = 16 g + c, g in 0..3, c in 0..15):
+//   S^T = K Q^T, one 16x16 block per 16 keys.  v_mfma_f64_16x16x4_f64 leaves
+//   D[g + 4r][c] in lane (g, c), register r, so a lane holds query c and keys
+//   g + 4r (r = 0..3) of the block.  The head-dim contraction is split into
+//   four contiguous quarters, quarter g fed by lane group g, so each lane
+//   reads its K row and Q row as contiguous 16-byte vectors.
+//   O^T = V^T P^T: the probabilities a lane already holds are exactly the B
+//   operand of v_mfma_f32_16x16x4_f32 (k index g <-> key g + 4r in step r),
+//   and lane (g, c) accumulates output channels 4g + r' of each 16-wide
+//   channel block for query c (that instruction's result layout is
+//   D[4g + r'][c]).  The rescale factor is therefore one scalar per lane.
+#include "attn_internal.h"
+#include "attn_device.h"
+
+#include <cmath>
+
+namespace attn {
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+template <int D, int BN, int WAVES, bool CAUSAL>
+__global__ __launch_bounds__(64 * WAVES)
+void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                         const float* __restrict__ V, float* __restrict__ O,
+                         float* __restrict__ LSE, int n_bh, int Sq, int Skv, double scale,
+                         int n_qt) {
+    constexpr int BM = 16 * WAVES;
+    constexpr int NT = 64 * WAVES;
+    constexpr int DQ = D / 4;      // head-dim quarter per lane group
+    constexpr int KP = D + 4;      // K row pitch in floats: 16-byte reads of 8 rows spread over all banks
+    constexpr int VP = D + 16;     // V row pitch: rows r and r+1 read by lanes 0-15 / 16-31 hit disjoint banks
+    constexpr int NKB = BN / 16;   // 16-key blocks per tile
+    constexpr int ND = D / 16;     // 16-wide output channel blocks
+    __shared__ __attribute__((aligned(16))) float sK[BN * KP];
+    __shared__ __attribute__((aligned(16))) float sV[BN * VP];
+
+    int bh, qt;
+    tile_coords(n_bh, n_qt, CAUSAL, bh, qt);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int off = Skv - Sq;
+    const int qi = qt * BM + wave * 16 + c;
+
+    const float* Qh = Q + (size_t)bh * Sq * D;
+    const float* Kh = K + (size_t)bh * Skv * D;
+    const float* Vh = V + (size_t)bh * Skv * D;
+
+    // Q^T operand, widened to fp64: q[qi][g*DQ + t].
+    double qreg[DQ];
+    if (qi < Sq) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(Qh + (size_t)qi * D + g * DQ);
+#pragma unroll
+        for (int t = 0; t < DQ / 4; ++t) {
+            f32x4 x = src[t];
+            qreg[4 * t + 0] = x[0];
+            qreg[4 * t + 1] = x[1];
+            qreg[4 * t + 2] = x[2];
+            qreg[4 * t + 3] = x[3];
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < DQ; ++t) qreg[t] = 0.0;
+    }
+
+    double m = -INFINITY;       // running maximum of scaled scores
+    float l = 0.f;              // this lane's part of the running normaliser
+    f32x4 acc[ND];              // unnormalised output accumulator
+#pragma unroll
+    for (int i = 0; i < ND; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int q_last = min(Sq, (qt + 1) * BM) - 1;
+    const int kv_end = kv_limit(q_last, Sq, Skv, CAUSAL);
+
+    for (int kv0 = 0; kv0 < kv_end; kv0 += BN) {
+        __syncthreads();
+        for (int e = tid; e < BN * (D / 4); e += NT) {
+            const int row = e / (D / 4);
+            const int c4 = e - row * (D / 4);
+            const int key = kv0 + row;
+            f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+            if (key < Skv) {
+                kx = *reinterpret_cast<const f32x4*>(Kh + (size_t)key * D + 4 * c4);
+                vx = *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + 4 * c4);
+            }
+            *reinterpret_cast<f32x4*>(&sK[row * KP + 4 * c4]) = kx;
+            *reinterpret_cast<f32x4*>(&sV[row * VP + 4 * c4]) = vx;
+        }
+        __syncthreads();
+
+        // scores s = scale * q.k in fp64, masked to -inf where invisible
+        double s[NKB][4];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            f64x4 st = {0.0, 0.0, 0.0, 0.0};
+            const float* krow = &sK[(kb * 16 + c) * KP + g * DQ];
+#pragma unroll
+            for (int t = 0; t < DQ; t += 4) {
+                f32x4 kx = *reinterpret_cast<const f32x4*>(krow + t);
+                st = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kx[0], qreg[t + 0], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kx[1], qreg[t + 1], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kx[2], qreg[t + 2], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kx[3], qreg[t + 3], st, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = kv0 + kb * 16 + g + 4 * r;
+                const bool vis = (j < Skv) && (!CAUSAL || j <= qi + off);
+                s[kb][r] = vis ? st[r] * scale : -INFINITY;
+            }
+        }
+
+        // m_new = max(m, max_j s_j) over the whole row (4 lane groups)
+        double mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmax(mx, s[kb][r]);
+        mx = fmax(mx, __shfl_xor(mx, 16));
+        mx = fmax(mx, __shfl_xor(mx, 32));
+        const double m_new = fmax(m, mx);
+        // reference point for the exponentials; 0 while the row has seen no key
+        const double m_ref = (m_new == -INFINITY) ? 0.0 : m_new;
+        const float alpha = exp2f((float)((m - m_ref) * kLog2e));   // 0 when m = -inf
+
+        float p[NKB][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[kb][r] = exp2f((float)((s[kb][r] - m_ref) * kLog2e));
+                psum += p[kb][r];
+            }
+        l = l * alpha + psum;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+        m = m_new;
+
+        // a += P V
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float* vrow = &sV[(kb * 16 + g + 4 * r) * VP + c];
+#pragma unroll
+                for (int i = 0; i < ND; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * i], p[kb][r], acc[i],
+                                                                  0, 0, 0);
+            }
+    }
+
+    // O = a / l, LSE = m + ln l; rows that saw no key keep O = 0, LSE = -inf
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (qi < Sq) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        float* orow = O + ((size_t)bh * Sq + qi) * D + 4 * g;
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+            *reinterpret_cast<f32x4*>(orow + 16 * i) = acc[i] * inv;
+        if (LSE != nullptr && g == 0)
+            LSE[(size_t)bh * Sq + qi] = lt > 0.f ? (float)(m + log((double)lt)) : -INFINITY;
+    }
+}
+
+template <int D, int BN, int WAVES>
+hipError_t launch_one(const Problem& p) {
+    constexpr int BM = 16 * WAVES;
+    const int n_bh = p.B * p.H;
+    const int n_qt = (p.Sq + BM - 1) / BM;
+    const dim3 grid((unsigned)(n_bh * n_qt));
+    const dim3 block(64 * WAVES);
+    const double scale = (double)p.scale;
+    const float* q = static_cast<const float*>(p.q);
+    const float* k = static_cast<const float*>(p.k);
+    const float* v = static_cast<const float*>(p.v);
+    float* o = static_cast<float*>(p.o);
+    if (p.causal)
+        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, true>), grid, block, 0, p.stream,
+                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt);
+    else
+        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, false>), grid, block, 0, p.stream,
+                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt);
+    return hipGetLastError();
+}
+
+template <int D, int BN>
+hipError_t by_waves(const Problem& p, int waves) {
+    switch (waves) {
+        case 1: return launch_one<D, BN, 1>(p);
+        case 2: return launch_one<D, BN, 2>(p);
+        case 4: return launch_one<D, BN, 4>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D>
+hipError_t by_bn(const Problem& p, int bn, int waves) {
+    switch (bn) {
+        case 16: return by_waves<D, 16>(p, waves);
+        case 32: return by_waves<D, 32>(p, waves);
+        case 64: return by_waves<D, 64>(p, waves);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool f32_tiles_supported(int d, int block_m, int block_n) {
+    const bool dm = d == 32 || d == 64 || d == 128;
+    const bool bm = block_m == 16 || block_m == 32 || block_m == 64;
+    const bool bn = block_n == 16 || block_n == 32 || block_n == 64;
+    return dm && bm && bn;
+}
+
+int f32_lds_bytes(int d, int /*block_m*/, int block_n) {
+    return block_n * ((d + 4) + (d + 16)) * (int)sizeof(float);
+}
+
+hipError_t launch_f32(const Problem& p, const Tiles& t) {
+    if (!f32_tiles_supported(p.d, t.block_m, t.block_n)) return hipErrorInvalidValue;
+    const int waves = t.block_m / 16;
+    switch (p.d) {
+        case 32: return by_bn<32>(p, t.block_n, waves);
+        case 64: return by_bn<64>(p, t.block_n, waves);
+        case 128: return by_bn<128>(p, t.block_n, waves);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn

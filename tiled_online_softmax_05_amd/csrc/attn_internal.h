@@ -1,0 +1,45 @@
+// Internal declarations shared by the kernel translation units and the C ABI
+// (host side).  Not installed; the public surface is include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace attn {
+
+// One launch's problem description, already validated by the C ABI.
+struct Problem {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;          // may be null
+    int B, H, Sq, Skv, d;
+    float scale;
+    bool causal;
+    int dtype;           // attn_dtype
+    hipStream_t stream;
+};
+
+// Tile shape chosen by the selector or forced by the caller.
+struct Tiles {
+    int block_m;   // query rows per workgroup
+    int block_n;   // key rows per K/V tile
+    int waves;     // 64-wide waves per workgroup
+    int lds_bytes; // LDS per workgroup
+};
+
+// Kernel families.  Each returns hipSuccess or the launch error, and
+// hipErrorInvalidValue when no kernel was built for (d, tiles).
+hipError_t launch_f32(const Problem& p, const Tiles& t);
+hipError_t launch_bf16(const Problem& p, const Tiles& t);
+// Fill O with zeros and LSE with -inf (Skv == 0: no row sees a key).
+hipError_t launch_empty_rows(const Problem& p);
+
+// Tile shapes that have a kernel, and their LDS footprint.
+bool f32_tiles_supported(int d, int block_m, int block_n);
+bool bf16_tiles_supported(int d, int block_m, int block_n);
+int f32_lds_bytes(int d, int block_m, int block_n);
+int bf16_lds_bytes(int d, int block_m, int block_n);
+
+}  // namespace attn
