@@ -100,6 +100,10 @@ int validate(const Problem& p) {
     if (bh > INT32_MAX) return fail(ATTN_ERR_INVALID_ARG, "B*H too large");
     if (bh * (int64_t)p.Sq > INT32_MAX || bh * (int64_t)p.Skv > INT32_MAX)
         return fail(ATTN_ERR_INVALID_ARG, "B*H*S exceeds 2^31 rows");
+    // one head's Q, K or V (at 4 bytes per element) must stay below 2 GiB:
+    // the kernels address a head with 32-bit byte offsets
+    if ((int64_t)p.Sq * p.d * 4 > INT32_MAX || (int64_t)p.Skv * p.d * 4 > INT32_MAX)
+        return fail(ATTN_ERR_INVALID_ARG, "sequence too long for one head (S*d*4 >= 2^31)");
     if (bh == 0 || p.Sq == 0) return ATTN_OK;
     if (p.q == nullptr || p.o == nullptr)
         return fail(ATTN_ERR_INVALID_ARG, "q and o must be non-null");

@@ -41,11 +41,21 @@ __device__ __forceinline__ int key_slot(int k) {
     return 8 * a + 4 * h + (k & 3);
 }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-    return (a & 0xffffu) | (b << 16);
+// s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Descriptor word 3 for raw (unswizzled) buffer access on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+
+// A buffer resource over [base, base + bytes): loads past the end return 0,
+// which is how the tails of Q, K and V read as zero rows without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferFlags);
 }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xffff0000u);
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
 template <int D, int BN, int WAVES, bool CAUSAL, bool OUT_F32>
@@ -62,6 +72,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     constexpr int NKB = BN / 32;       // 32-key blocks per tile
     constexpr int ND = D / 32;         // 32-channel output blocks
     constexpr int DCH = D / 8;         // 16-byte chunks per K/V row
+    constexpr int ROWB = D * 2;        // bytes per K/V row
     constexpr int K_ITEMS = BN * DCH;              // one 16-byte chunk each
     constexpr int V_ITEMS = (BN / 4) * DCH;        // 4 keys x 8 channels each
     constexpr int K_PER = (K_ITEMS + NT - 1) / NT;
@@ -86,15 +97,19 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const __bf16* Kh = K + (size_t)bh * Skv * D;
     const __bf16* Vh = V + (size_t)bh * Skv * D;
 
-    // Q^T operand: lane holds q[qi][16 ks + 8 h .. +7]
+    // Q^T operand: lane holds q[qi][16 ks + 8 h .. +7]; rows past Sq read 0
     bf16x8 qop[KS];
-    if (qi < Sq) {
-        const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)qi * D + 8 * h);
+    {
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Qh, (uint32_t)Sq * ROWB);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[ks] = src[2 * ks];
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qop[ks] = bf16x8{};
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 x = buffer_load16(rq, (uint32_t)qi * ROWB + 32 * ks + 16 * h);
+            qop[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+        // Retire the Q loads here, on every path: vmcnt is in-order, and Q
+        // loads still in flight at the loop entry would make every tile wait
+        // for its own K/V prefetch before the first MFMA.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     float m = -INFINITY;     // running max of scale*log2(e)*s
@@ -105,35 +120,35 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
     const int q_last = min(Sq, (qt + 1) * BM) - 1;
     const int kv_end = kv_limit(q_last, Sq, Skv, CAUSAL);
+    // last key this lane's query may see (for the masked tiles)
+    const int lim = CAUSAL ? min(Skv - 1, qi + off) : Skv - 1;
 
     // ---- K/V tile staging: HBM -> registers -> LDS ----
+    // One descriptor per head; the tile offset rides in the per-lane offset so
+    // rows at or past Skv fall outside the descriptor's range and read 0.
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(Kh, (uint32_t)Skv * ROWB);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(Vh, (uint32_t)Skv * ROWB);
+    constexpr bool K_FULL = K_ITEMS % NT == 0;   // every thread has K_PER items
+    constexpr bool V_FULL = V_ITEMS % NT == 0;
     u32x4 kreg[K_PER];
     u32x4 vreg[V_PER][4];
     auto load_tile = [&](int kv0) {
+        const uint32_t tile_off = (uint32_t)kv0 * ROWB;
 #pragma unroll
         for (int i = 0; i < K_PER; ++i) {
             const int e = tid + i * NT;
-            kreg[i] = u32x4{0u, 0u, 0u, 0u};
-            if (e < K_ITEMS) {
-                const int row = e / DCH, ch = e - (e / DCH) * DCH;
-                const int key = kv0 + row;
-                if (key < Skv)
-                    kreg[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + 8 * ch);
-            }
+            const int row = e / DCH, ch = e % DCH;
+            if (K_FULL || e < K_ITEMS)
+                kreg[i] = buffer_load16(rk, tile_off + row * ROWB + 16 * ch);
         }
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
             const int e = tid + i * NT;
+            const int kg = e / DCH, ch = e % DCH;
+            if (V_FULL || e < V_ITEMS) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) vreg[i][t] = u32x4{0u, 0u, 0u, 0u};
-            if (e < V_ITEMS) {
-                const int kg = e / DCH, ch = e - (e / DCH) * DCH;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int key = kv0 + 4 * kg + t;
-                    if (key < Skv)
-                        vreg[i][t] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + 8 * ch);
-                }
+                for (int t = 0; t < 4; ++t)
+                    vreg[i][t] = buffer_load16(rv, tile_off + (4 * kg + t) * ROWB + 16 * ch);
             }
         }
     };
@@ -141,8 +156,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 #pragma unroll
         for (int i = 0; i < K_PER; ++i) {
             const int e = tid + i * NT;
-            if (e < K_ITEMS) {
-                const int row = e / DCH, ch = e - (e / DCH) * DCH;
+            if (K_FULL || e < K_ITEMS) {
+                const int row = e / DCH, ch = e % DCH;
                 const int slot = (row & ~31) + key_slot(row & 31);
                 *reinterpret_cast<u32x4*>(&sK[slot * KP + 8 * ch]) = kreg[i];
             }
@@ -150,16 +165,16 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
             const int e = tid + i * NT;
-            if (e < V_ITEMS) {
-                const int kg = e / DCH, ch = e - (e / DCH) * DCH;
-                // channel 8 ch + 2 w (+1) of keys 4 kg .. 4 kg + 3
+            if (V_FULL || e < V_ITEMS) {
+                const int kg = e / DCH, ch = e % DCH;
+                // channels 8 ch + 2 w and 8 ch + 2 w + 1 of keys 4 kg .. 4 kg + 3
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     u32x2 lo, hi;
-                    lo[0] = pack_lo(vreg[i][0][w], vreg[i][1][w]);
-                    lo[1] = pack_lo(vreg[i][2][w], vreg[i][3][w]);
-                    hi[0] = pack_hi(vreg[i][0][w], vreg[i][1][w]);
-                    hi[1] = pack_hi(vreg[i][2][w], vreg[i][3][w]);
+                    lo[0] = __builtin_amdgcn_perm(vreg[i][1][w], vreg[i][0][w], 0x05040100u);
+                    lo[1] = __builtin_amdgcn_perm(vreg[i][3][w], vreg[i][2][w], 0x05040100u);
+                    hi[0] = __builtin_amdgcn_perm(vreg[i][1][w], vreg[i][0][w], 0x07060302u);
+                    hi[1] = __builtin_amdgcn_perm(vreg[i][3][w], vreg[i][2][w], 0x07060302u);
                     const int ch0 = 8 * ch + 2 * w;
                     *reinterpret_cast<u32x2*>(&sVt[ch0 * VP + 4 * kg]) = lo;
                     *reinterpret_cast<u32x2*>(&sVt[(ch0 + 1) * VP + 4 * kg]) = hi;
@@ -194,13 +209,13 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         // ---- mask: only tiles crossing the key end or the causal diagonal ----
         const bool need_mask = (kv0 + BN > Skv) || (CAUSAL && kv0 + BN - 1 > q0w + off);
         if (need_mask) {
+            const int base = lim - kv0 - 8 * h;     // visible iff key offset <= base
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int j = kv0 + kb * 32 + 16 * (r >> 3) + 8 * h + (r & 7);
-                    const bool vis = (j < Skv) && (!CAUSAL || j <= qi + off);
-                    if (!vis) st[kb][r] = -INFINITY;
+                    const int jo = kb * 32 + 16 * (r >> 3) + (r & 7);
+                    if (jo > base) st[kb][r] = -INFINITY;
                 }
         }
 
@@ -213,7 +228,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m, mx * sl2);
         const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m - m_ref);        // 0 while m = -inf
+        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);   // 0 while m = -inf
 
         bf16x8 pb[NKB][2];
         float psum = 0.f;
@@ -224,15 +239,18 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                 f32x8 pf;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float pv = exp2f(fmaf(st[kb][8 * half + j], sl2, -m_ref));
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][8 * half + j], sl2, -m_ref));
                     pf[j] = pv;
                     psum += pv;
                 }
                 pb[kb][half] = __builtin_convertvector(pf, bf16x8);
             }
         l = l * alpha + psum;
+        // the accumulator changes only where the maximum rose (alpha != 1)
+        if (__any(m_new > m)) {
 #pragma unroll
-        for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+            for (int i = 0; i < ND; ++i) acc[i] *= alpha;
+        }
         m = m_new;
 
         // ---- O^T += V^T P^T ----
