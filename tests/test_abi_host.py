@@ -46,10 +46,10 @@ def test_version(lib):
     ((64, 512, 512, 8, B.F32, 0), (16, 64, 1)),
     ((32, 8, 1000, 6, B.F32, 1), (16, 64, 1)),
     ((32, 8, 16, 6, B.F32, 0), (16, 16, 1)),
-    ((128, 4096, 4096, 32, B.BF16, 1), (128, 64, 4)),
-    ((128, 32768, 32768, 64, B.BF16, 1), (128, 64, 4)),
-    ((128, 256, 256, 2, B.BF16, 1), (64, 64, 2)),
-    ((64, 4096, 4096, 32, B.BF16_OUT_F32, 0), (128, 64, 4)),
+    ((128, 4096, 4096, 32, B.BF16, 1), (128, 32, 4)),
+    ((128, 32768, 32768, 64, B.BF16, 1), (128, 32, 4)),
+    ((128, 256, 256, 2, B.BF16, 1), (64, 32, 2)),
+    ((64, 4096, 4096, 32, B.BF16_OUT_F32, 0), (128, 32, 4)),
 ])
 def test_selector(lib, args, want):
     bm, bn, waves, lds = B.select_tiles(*args)

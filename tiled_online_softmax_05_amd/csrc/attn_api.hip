@@ -75,7 +75,9 @@ int select(int d, int Sq, int Skv, int BH, int dtype, Tiles* t) {
     if (!(d == 64 || d == 128))
         return fail(ATTN_ERR_UNSUPPORTED, "bf16 head dim %d not built (64, 128)", d);
     int bm = (wgs(128) >= kCUs && Sq > 64) ? 128 : 64;
-    int bn = Skv > 32 ? 64 : 32;
+    // 32-key tiles: the software-pipelined kernel holds two score tiles in
+    // registers, and 64-key tiles would not fit at two waves per SIMD
+    int bn = 32;
     t->block_m = bm;
     t->block_n = bn;
     t->waves = bm / 32;

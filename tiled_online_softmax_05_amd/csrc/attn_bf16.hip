@@ -18,27 +18,37 @@
 // block are stored in LDS in the order sigma^-1, chosen so that D row
 // 8a + 4h + b carries key 16 (a/2) + 8 h + 4 (a%2) + b: a lane then holds 8
 // consecutive keys per 16-key step, which is exactly the B operand layout
-// of the next contraction O^T = V^T P^T.  V is stored transposed in LDS
-// ([channel][key]) so the A operand of that contraction is one 16-byte read.
+// of the next contraction O^T = V^T P^T.
 //
 // Exponentials are base 2 with scale * log2(e) folded into one FMA; the
-// running maximum m is kept in that scaled base-2 domain.
+// running reference m is kept in that scaled base-2 domain.  It follows the
+// row maximum lazily (see kSlack): it is raised to a tile's maximum only when
+// that maximum exceeds it by more than kSlack, and whenever it is raised both
+// l and the accumulator are rescaled by 2^(m_old - m_new) -- the online
+// normalisation with a relaxed choice of reference point, which gives the
+// same O and LSE up to rounding.
 #include "attn_internal.h"
 #include "attn_device.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace attn {
 namespace {
 
 constexpr float kLog2ef = 1.44269504088896341f;
+// Slack of the running reference, in base-2 exponent units: the reference
+// point m moves (and l and a are rescaled by 2^(m_old - m_new)) only when a
+// tile's maximum exceeds it by more than this, so probabilities stay below
+// 2^kSlack = 256 and most tiles skip the accumulator rescale.
+constexpr float kSlack = 8.f;
 constexpr float kLn2f = 0.693147180559945309f;
 
-// LDS row of key k (0..31) inside its 32-key block (inverse of sigma).
-__device__ __forceinline__ int key_slot(int k) {
-    const int a = 2 * (k >> 4) + ((k >> 2) & 1);
-    const int h = (k >> 3) & 1;
-    return 8 * a + 4 * h + (k & 3);
+// Key held by LDS row r (0..31) of a 32-key block: D row 8a + 4h + b of the
+// score contraction must carry key 16 (a/2) + 8 h + 4 (a%2) + b.
+__device__ __forceinline__ int sigma(int r) {
+    const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
+    return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
 // s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
@@ -58,6 +68,32 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
+
+__device__ __forceinline__ float other_half_max(float x) {
+    // v_permlane32_swap: lane l (< 32) receives lane l + 32 and vice versa
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float other_half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Software-pipelined main loop.  Step j holds K_{j+1} and V_j in LDS (two
+// buffers each, chosen by the parity of j) and the raw scores S_j in
+// registers.  Phase A: the matrix cores compute S_{j+1} = K_{j+1} Q^T while
+// the VALU runs the online-softmax update of S_j (row max, rescale factor,
+// exponentials, bf16 packing).  Phase B: O^T += V_j^T P_j on the matrix cores
+// while the VALU rescales the accumulator block by block and sums the
+// probabilities.  K_{j+2} and V_{j+1} travel HBM -> LDS by DMA during the step
+// into the buffers freed by step j - 1; one workgroup barrier per step
+// separates a buffer's last read from its next write.  Within a phase the
+// instruction order is fixed by hand (sched_barrier fences): every MFMA
+// operand is read from LDS two MFMAs ahead of its use, and the VALU work is
+// cut into slices placed between consecutive MFMAs.
 template <int D, int BN, int WAVES, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -66,21 +102,37 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                           int n_qt) {
     constexpr int BM = 32 * WAVES;
     constexpr int NT = 64 * WAVES;
-    constexpr int KP = D + 8;          // sK row pitch (bf16 elements)
-    constexpr int VP = BN + 8;         // sVt row pitch (bf16 elements)
     constexpr int KS = D / 16;         // k-steps of the score contraction
     constexpr int NKB = BN / 32;       // 32-key blocks per tile
     constexpr int ND = D / 32;         // 32-channel output blocks
     constexpr int DCH = D / 8;         // 16-byte chunks per K/V row
     constexpr int ROWB = D * 2;        // bytes per K/V row
-    constexpr int K_ITEMS = BN * DCH;              // one 16-byte chunk each
-    constexpr int V_ITEMS = (BN / 4) * DCH;        // 4 keys x 8 channels each
-    constexpr int K_PER = (K_ITEMS + NT - 1) / NT;
-    constexpr int V_PER = (V_ITEMS + NT - 1) / NT;
+    constexpr int CHUNKS = BN * DCH;   // 16-byte chunks per K or V tile
+    constexpr int PER = CHUNKS / NT;   // chunks each thread moves per tile
+    constexpr int NA = NKB * KS;       // MFMAs of phase A (scores)
+    constexpr int NB = 2 * NKB * ND;   // MFMAs of phase B (P.V)
+    constexpr int NV = 16 * NKB;       // scores per lane per tile
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(CHUNKS % NT == 0, "every lane moves the same number of chunks");
+    static_assert(DCH == 8 || DCH == 16, "K swizzle covers 8 or 16 chunks per row");
+    static_assert(NA >= 4 && NB >= ND + 1, "schedule needs a few MFMAs per phase");
 
-    __shared__ __attribute__((aligned(16))) __bf16 sK[BN * KP];
-    __shared__ __attribute__((aligned(16))) __bf16 sVt[D * VP];
+    // Separate arrays (not one indexed by a runtime parity) let the compiler
+    // see that the DMA into one buffer never aliases reads of the other.
+    __shared__ __attribute__((aligned(16))) __bf16 sK0[BN * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sK1[BN * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sV0[BN * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sV1[BN * D];
+
+    // K layout in LDS: unpadded rows of DCH 16-byte chunks; chunk q of row r
+    // sits at position q ^ k_swz(r).  An operand read (16 lanes = 16
+    // consecutive rows, one chunk) then touches 16 distinct 16-byte bank
+    // groups of the 64-bank LDS.
+    auto k_swz = [](int r) { return DCH == 16 ? (r & 15) : ((r >> 1) & 7); };
+    // V layout in LDS: row = key, chunk q of row key at q ^ v_swz(key).  The
+    // transposing operand read of 32 lanes covers 4 keys x 4 chunks; the
+    // swizzle puts those 16 chunks in 16 distinct bank groups.
+    auto v_swz = [](int key) { return DCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); };
 
     int bh, qt;
     tile_coords(n_bh, n_qt, CAUSAL, bh, qt);
@@ -108,7 +160,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         }
         // Retire the Q loads here, on every path: vmcnt is in-order, and Q
         // loads still in flight at the loop entry would make every tile wait
-        // for its own K/V prefetch before the first MFMA.
+        // for its own K/V loads before the first MFMA.
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
@@ -120,95 +172,72 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
     const int q_last = min(Sq, (qt + 1) * BM) - 1;
     const int kv_end = kv_limit(q_last, Sq, Skv, CAUSAL);
+    const int n_tiles = (kv_end + BN - 1) / BN;
     // last key this lane's query may see (for the masked tiles)
     const int lim = CAUSAL ? min(Skv - 1, qi + off) : Skv - 1;
 
-    // ---- K/V tile staging: HBM -> registers -> LDS ----
+    // ---- K/V staging: HBM -> LDS by DMA ----
     // One descriptor per head; the tile offset rides in the per-lane offset so
     // rows at or past Skv fall outside the descriptor's range and read 0.
+    // Slot S = i * NT + tid (16 bytes) of LDS row S / DCH holds chunk
+    // (S % DCH) ^ swizzle(row) of that row's key.
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(Kh, (uint32_t)Skv * ROWB);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(Vh, (uint32_t)Skv * ROWB);
-    constexpr bool K_FULL = K_ITEMS % NT == 0;   // every thread has K_PER items
-    constexpr bool V_FULL = V_ITEMS % NT == 0;
-    u32x4 kreg[K_PER];
-    u32x4 vreg[V_PER][4];
-    auto load_tile = [&](int kv0) {
-        const uint32_t tile_off = (uint32_t)kv0 * ROWB;
+    auto load_k = [&](int kv0, __bf16* dst) {
 #pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int e = tid + i * NT;
-            const int row = e / DCH, ch = e % DCH;
-            if (K_FULL || e < K_ITEMS)
-                kreg[i] = buffer_load16(rk, tile_off + row * ROWB + 16 * ch);
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int e = tid + i * NT;
-            const int kg = e / DCH, ch = e % DCH;
-            if (V_FULL || e < V_ITEMS) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    vreg[i][t] = buffer_load16(rv, tile_off + (4 * kg + t) * ROWB + 16 * ch);
-            }
+        for (int i = 0; i < PER; ++i) {
+            const int S = i * NT + tid;
+            const int row = S / DCH;
+            const int chunk = (S % DCH) ^ k_swz(row);
+            const int key = (row & ~31) + sigma(row & 31);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (__attribute__((address_space(3))) void*)(dst + (i * NT + wave * 64) * 8), 16,
+                (uint32_t)(kv0 + key) * ROWB + 16 * chunk, 0, 0, 0);
         }
     };
-    auto store_tile = [&]() {
+    auto load_v = [&](int kv0, __bf16* dst) {
 #pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int e = tid + i * NT;
-            if (K_FULL || e < K_ITEMS) {
-                const int row = e / DCH, ch = e % DCH;
-                const int slot = (row & ~31) + key_slot(row & 31);
-                *reinterpret_cast<u32x4*>(&sK[slot * KP + 8 * ch]) = kreg[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int e = tid + i * NT;
-            if (V_FULL || e < V_ITEMS) {
-                const int kg = e / DCH, ch = e % DCH;
-                // channels 8 ch + 2 w and 8 ch + 2 w + 1 of keys 4 kg .. 4 kg + 3
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    u32x2 lo, hi;
-                    lo[0] = __builtin_amdgcn_perm(vreg[i][1][w], vreg[i][0][w], 0x05040100u);
-                    lo[1] = __builtin_amdgcn_perm(vreg[i][3][w], vreg[i][2][w], 0x05040100u);
-                    hi[0] = __builtin_amdgcn_perm(vreg[i][1][w], vreg[i][0][w], 0x07060302u);
-                    hi[1] = __builtin_amdgcn_perm(vreg[i][3][w], vreg[i][2][w], 0x07060302u);
-                    const int ch0 = 8 * ch + 2 * w;
-                    *reinterpret_cast<u32x2*>(&sVt[ch0 * VP + 4 * kg]) = lo;
-                    *reinterpret_cast<u32x2*>(&sVt[(ch0 + 1) * VP + 4 * kg]) = hi;
-                }
-            }
+        for (int i = 0; i < PER; ++i) {
+            const int S = i * NT + tid;
+            const int key = S / DCH;
+            const int chunk = (S % DCH) ^ v_swz(key);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (__attribute__((address_space(3))) void*)(dst + (i * NT + wave * 64) * 8), 16,
+                (uint32_t)(kv0 + key) * ROWB + 16 * chunk, 0, 0, 0);
         }
     };
 
-    if (kv_end > 0) {
-        load_tile(0);
-        store_tile();
-    }
-    __syncthreads();
-
-    for (int kv0 = 0; kv0 < kv_end; kv0 += BN) {
-        const bool has_next = kv0 + BN < kv_end;
-        if (has_next) load_tile(kv0 + BN);
-
-        // ---- S^T = K Q^T (raw scores, fp32) ----
-        f32x16 st[NKB];
+    // ---- operand reads ----
+    // phase-A MFMA t: key block kb = t % NKB, k-step ks = t / NKB (the two
+    // accumulators alternate)
+    auto k_operand = [&](const __bf16* sk, int t) -> bf16x8 {
+        const int kb = t % NKB, ks = t / NKB;
+        const int row = kb * 32 + c;
+        return *reinterpret_cast<const bf16x8*>(sk + row * D + 8 * ((2 * ks + h) ^ k_swz(row)));
+    };
+    // phase-B MFMA t: k-step s = t / ND (keys 16 s .. 16 s + 15), channel
+    // block i = t % ND; two transposing reads, keys 8 h + 4 u .. + 3
+    const int g16 = lane & 15;
+    const int cblk = lane & 16;
+    auto v_operand = [&](const __bf16* sv, int t) -> bf16x8 {
+        const int s = t / ND, i = t % ND;
+        bf16x4 part[2];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            st[kb] = f32x16{};
-            const __bf16* krow = &sK[(kb * 32 + c) * KP + 8 * h];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
-                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], st[kb], 0, 0, 0);
-            }
+        for (int u = 0; u < 2; ++u) {
+            const int key = 16 * s + 8 * h + 4 * u + (g16 >> 2);
+            const int d = 32 * i + cblk + 4 * (g16 & 3);
+            const __bf16* src = sv + key * D + 8 * ((d >> 3) ^ v_swz(key)) + (d & 7);
+            part[u] = __builtin_bit_cast(
+                bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4*)(src)));
         }
+        return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 
-        // ---- mask: only tiles crossing the key end or the causal diagonal ----
-        const bool need_mask = (kv0 + BN > Skv) || (CAUSAL && kv0 + BN - 1 > q0w + off);
-        if (need_mask) {
+    auto mask = [&](int kv0, f32x16* st) {
+        // only tiles crossing the key end or the causal diagonal
+        const bool need = (kv0 + BN > Skv) || (CAUSAL && kv0 + BN - 1 > q0w + off);
+        if (need) {
             const int base = lim - kv0 - 8 * h;     // visible iff key offset <= base
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -218,65 +247,156 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                     if (jo > base) st[kb][r] = -INFINITY;
                 }
         }
+    };
 
-        // ---- online softmax update ----
-        float mx = -INFINITY;
+    // Phase A for scores st (tile j) with the next tile's K in sk: returns
+    // the accumulator rescale factor (and whether any lane of the wave needs
+    // it); fills sn (scores of tile j + 1) when NEXT and the bf16
+    // probabilities pb, and updates m and l.
+    auto phase_a = [&](auto NEXT, const __bf16* sk, const f32x16* st, f32x16* sn,
+                       bf16x8 (*pb)[2], bool& rescale) -> float {
+        constexpr bool next = decltype(NEXT)::value;
+        bf16x8 ka[3];
+        if constexpr (next) {
+            ka[0] = k_operand(sk, 0);
+            ka[1] = k_operand(sk, 1);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+            for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
+        }
+        float mx = -INFINITY, m_ref = 0.f, alpha = 1.f, psum = 0.f;
+        f32x8 v8;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx * sl2);
-        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);   // 0 while m = -inf
-
-        bf16x8 pb[NKB][2];
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f32x8 pf;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][8 * half + j], sl2, -m_ref));
-                    pf[j] = pv;
-                    psum += pv;
-                }
-                pb[kb][half] = __builtin_convertvector(pf, bf16x8);
+        for (int t = 0; t < NA; ++t) {
+            if constexpr (next) {
+                if (t + 2 < NA) ka[(t + 2) % 3] = k_operand(sk, t + 2);
+                const int kb = t % NKB, ks = t / NKB;
+                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qop[ks], sn[kb], 0, 0, 0);
             }
+            if (t == 0) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+            }
+            if (t == 1) {
+                mx = other_half_max(mx);
+                const float mt = mx * sl2;              // tile max, scaled base-2 domain
+                const bool grow = mt > m + kSlack;      // true on the first visible tile
+                // 2^(m - mt): 0 when m = -inf; no rescale (1) while m stays put
+                alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+                m = grow ? mt : m;
+                m_ref = (m == -INFINITY) ? 0.f : m;     // 0 while the row has seen no key
+                rescale = __any(grow);
+            }
+            if (t >= 2) {
+                // exponentials of values [e0, e1), packed to bf16 in groups of 8
+                const int e0 = (t - 2) * NV / (NA - 2), e1 = (t - 1) * NV / (NA - 2);
+#pragma unroll
+                for (int e = e0; e < e1; ++e) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(st[e / 16][e % 16], sl2, -m_ref));
+                    v8[e & 7] = pv;
+                    psum += pv;
+                    if ((e & 7) == 7) pb[e / 16][(e / 8) & 1] = __builtin_convertvector(v8, bf16x8);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         l = l * alpha + psum;
-        // the accumulator changes only where the maximum rose (alpha != 1)
-        if (__any(m_new > m)) {
+        return alpha;
+    };
+
+    // Phase B: rescale the accumulator if the reference moved, then
+    // O^T += V^T P^T from sv.
+    auto phase_b = [&](const __bf16* __restrict__ sv, const bf16x8 (*pb)[2], float alpha,
+                       bool rescale) {
+        if (rescale) {
 #pragma unroll
             for (int i = 0; i < ND; ++i) acc[i] *= alpha;
         }
-        m = m_new;
-
-        // ---- O^T += V^T P^T ----
+        bf16x8 va[3];
+        va[0] = v_operand(sv, 0);
+        va[1] = v_operand(sv, 1);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int kcol = 32 * kb + 16 * half + 8 * h;
-#pragma unroll
-                for (int i = 0; i < ND; ++i) {
-                    const bf16x8 a =
-                        *reinterpret_cast<const bf16x8*>(&sVt[(32 * i + c) * VP + kcol]);
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][half], acc[i],
-                                                                     0, 0, 0);
-                }
-            }
-
-        __syncthreads();
-        if (has_next) {
-            store_tile();
-            __syncthreads();
+        for (int t = 0; t < NB; ++t) {
+            const int s = t / ND, i = t % ND;
+            if (t + 2 < NB) va[(t + 2) % 3] = v_operand(sv, t + 2);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], pb[s / 2][s % 2], acc[i],
+                                                             0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    using std::integral_constant;
+    // Steady-state step j.  The four buffers arrive as distinct restrict
+    // pointers: once inlined, every LDS access and DMA in the step carries
+    // scoped no-alias metadata, which lets the compiler see that the DMA into
+    // the free buffers never overlaps the operand reads of the busy ones (the
+    // transposing read otherwise waits for all DMA in flight).
+    auto step = [&](int j, f32x16* st, const __bf16* __restrict__ k_next,
+                    __bf16* __restrict__ k_free, const __bf16* __restrict__ v_cur,
+                    __bf16* __restrict__ v_free) {
+        const int kv0 = j * BN;
+        load_k(kv0 + 2 * BN, k_free);           // K_{j+2}: zero rows or unused past the end
+        load_v(kv0 + BN, v_free);               // V_{j+1}
+        mask(kv0, st);
+        f32x16 sn[NKB];
+        bf16x8 pb[NKB][2];
+        bool rescale;
+        const float alpha = phase_a(integral_constant<bool, true>{}, k_next, st, sn, pb, rescale);
+        phase_b(v_cur, pb, alpha, rescale);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) st[kb] = sn[kb];
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // K_{j+2}, V_{j+1} have landed
+        __syncthreads();
+    };
+    auto last = [&](auto P, int j, f32x16* st) {
+        constexpr int p = decltype(P)::value;
+        mask(j * BN, st);
+        bf16x8 pb[NKB][2];
+        bool rescale;
+        const float alpha =
+            phase_a(integral_constant<bool, false>{}, nullptr, st, nullptr, pb, rescale);
+        phase_b(p ? sV1 : sV0, pb, alpha, rescale);
+    };
+
+    if (n_tiles > 0) {
+        // ---- prologue: S_0 from K_0; K_1 and V_0 into LDS ----
+        load_k(0, sK0);
+        load_v(0, sV0);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);      // K_0 and V_0 have landed
+        __syncthreads();
+        load_k(BN, sK1);
+        f32x16 st[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            st[kb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(sK0, ks * NKB + kb),
+                                                                 qop[ks], st[kb], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+
+        // ---- steady state: tiles 0 .. n_tiles - 2, two per trip ----
+        int j = 0;
+        for (; j + 2 < n_tiles; j += 2) {
+            step(j, st, sK1, sK0, sV0, sV1);
+            step(j + 1, st, sK0, sK1, sV1, sV0);
+        }
+        if (j + 1 < n_tiles) {
+            step(j, st, sK1, sK0, sV0, sV1);
+            ++j;
+        }
+        // ---- last tile (index j = n_tiles - 1) ----
+        if (j & 1)
+            last(integral_constant<int, 1>{}, j, st);
+        else
+            last(integral_constant<int, 0>{}, j, st);
     }
 
     // ---- epilogue: O = a / l, LSE = ln 2 * (m + log2 l) ----
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = other_half_sum(l);
     if (qi < Sq) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const size_t obase = ((size_t)bh * Sq + qi) * D;
@@ -336,7 +456,7 @@ bool bf16_tiles_supported(int d, int block_m, int block_n) {
 }
 
 int bf16_lds_bytes(int d, int /*block_m*/, int block_n) {
-    return (block_n * (d + 8) + d * (block_n + 8)) * 2;
+    return 2 * 2 * block_n * d * 2;   // K and V, two buffers each
 }
 
 hipError_t launch_bf16(const Problem& p, const Tiles& t) {
