@@ -97,7 +97,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * function on "Verify tiled attention").  block_m = block_n = 0 means "use
  * the selector".  Built shapes:
  *   ATTN_F32            block_m in {16, 32, 64},  block_n in {16, 32, 64}
- *   ATTN_BF16[_OUT_F32] block_m in {64, 128},     block_n in {32, 64}
+ *   ATTN_BF16[_OUT_F32] block_m in {64, 128},     block_n in {32, 64},
+ *                       and block_m = 256 with block_n = 32 when d = 128
  * Any other pair returns ATTN_ERR_UNSUPPORTED.
  */
 int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,

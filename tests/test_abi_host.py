@@ -50,6 +50,8 @@ def test_version(lib):
     ((128, 32768, 32768, 64, B.BF16, 1), (128, 32, 4)),
     ((128, 256, 256, 2, B.BF16, 1), (64, 32, 2)),
     ((64, 4096, 4096, 32, B.BF16_OUT_F32, 0), (128, 32, 4)),
+    ((128, 4096, 4096, 16, B.BF16, 1), (128, 32, 4)),
+    ((128, 1024, 1024, 2, B.BF16, 1), (64, 32, 2)),
 ])
 def test_selector(lib, args, want):
     bm, bn, waves, lds = B.select_tiles(*args)

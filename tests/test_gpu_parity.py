@@ -130,9 +130,11 @@ def test_longctx_h64_s32768_d128_sampled(longctx, out_dtype):
 # ------------------------------------------------------------------ smaller bf16 shapes, whole output
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("tiles", [(128, 64), (128, 32), (64, 64), (64, 32), None],
-                         ids=["128x64", "128x32", "64x64", "64x32", "selector"])
+@pytest.mark.parametrize("tiles", [(256, 32), (128, 64), (128, 32), (64, 64), (64, 32), None],
+                         ids=["256x32", "128x64", "128x32", "64x64", "64x32", "selector"])
 def test_bf16_ragged_tiles(d, causal, tiles):
+    if tiles == (256, 32) and d != 128:
+        pytest.skip("256-row tiles are built for d = 128 only")
     q, k, v = random_tensors(1, 3, 300, 333, d, "bf16", "uniform0.8", seed=17 + d)
     log(f"bf16 ragged d={d} causal={causal} tiles={tiles}")
     check_full(q, k, v, causal, tiles=tiles, what=f"bf16 300x333 d={d}")

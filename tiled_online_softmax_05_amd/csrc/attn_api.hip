@@ -57,7 +57,7 @@ int out_bytes(int dtype) { return dtype == ATTN_BF16 ? 2 : 4; }
 // The selector.  Query rows per workgroup shrink until the grid has at
 // least one workgroup per compute unit (256 on MI355X) or the smallest
 // shape is reached; key rows per tile follow the key length.
-int select(int d, int Sq, int Skv, int BH, int dtype, Tiles* t) {
+int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
     constexpr long kCUs = 256;
     auto wgs = [&](int bm) { return (long)BH * ((Sq + bm - 1) / bm); };
     if (dtype == ATTN_F32) {
@@ -74,9 +74,17 @@ int select(int d, int Sq, int Skv, int BH, int dtype, Tiles* t) {
     }
     if (!(d == 64 || d == 128))
         return fail(ATTN_ERR_UNSUPPORTED, "bf16 head dim %d not built (64, 128)", d);
-    int bm = (wgs(128) >= kCUs && Sq > 64) ? 128 : 64;
-    // 32-key tiles: the software-pipelined kernel holds two score tiles in
-    // registers, and 64-key tiles would not fit at two waves per SIMD
+    // Workgroups of 128 query rows (four waves, two workgroups per CU) when
+    // that gives every CU a workgroup, else 64; causal workgroups take a heavy
+    // and a light query tile each.  32-key tiles: the pipelined kernel holds
+    // two score tiles in registers, and 64-key tiles would not fit at two
+    // waves per SIMD.  (256-row workgroups of eight waves are built for d=128
+    // but measured no faster.)
+    auto items = [&](int bm) {
+        const long n_qt = (Sq + bm - 1) / bm;
+        return (long)BH * (causal ? (n_qt + 1) / 2 : n_qt);
+    };
+    int bm = items(128) >= kCUs ? 128 : 64;
     int bn = 32;
     t->block_m = bm;
     t->block_n = bn;
@@ -133,7 +141,7 @@ int run(const Problem& p, int block_m, int block_n) {
     if (bh == 0 || p.Sq == 0) return ok();
     Tiles t{};
     if (block_m == 0 && block_n == 0) {
-        st = select(p.d, p.Sq, p.Skv, bh, p.dtype, &t);
+        st = select(p.d, p.Sq, p.Skv, bh, p.dtype, p.causal, &t);
         if (st != ATTN_OK) return st;
     } else {
         const bool sup = p.dtype == ATTN_F32 ? f32_tiles_supported(p.d, block_m, block_n)
@@ -192,7 +200,7 @@ int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal, int
     if (d <= 0 || Sq < 0 || Skv < 0 || BH < 0)
         return attn::fail(ATTN_ERR_INVALID_ARG, "negative or zero size");
     attn::Tiles t{};
-    const int st = attn::select(d, Sq, Skv, BH, dtype, &t);
+    const int st = attn::select(d, Sq, Skv, BH, dtype, causal == 1, &t);
     if (st != ATTN_OK) return st;
     if (block_m) *block_m = t.block_m;
     if (block_n) *block_n = t.block_n;

@@ -51,8 +51,10 @@ __device__ __forceinline__ int sigma(int r) {
     return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
-// s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima.
+// s_waitcnt immediates: vmcnt = n (6 bits on gfx9: [3:0] and [15:14]),
+// expcnt and lgkmcnt left at their maxima.
 constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Descriptor word 3 for raw (unswizzled) buffer access on gfx9-family parts.
 constexpr int kBufferFlags = 0x00020000;
@@ -68,6 +70,14 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
+
+// Empty register-level barrier: makes x an output of a volatile statement at
+// this point, so IR passes cannot sink the code producing x past it (the
+// sched_barrier fences only order machine instructions).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+    asm volatile("" : "+v"(x));
+}
 
 __device__ __forceinline__ float other_half_max(float x) {
     // v_permlane32_swap: lane l (< 32) receives lane l + 32 and vice versa
@@ -117,12 +127,19 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     static_assert(DCH == 8 || DCH == 16, "K swizzle covers 8 or 16 chunks per row");
     static_assert(NA >= 4 && NB >= ND + 1, "schedule needs a few MFMAs per phase");
 
-    // Separate arrays (not one indexed by a runtime parity) let the compiler
-    // see that the DMA into one buffer never aliases reads of the other.
+    // Three buffers each for K and V: K_t lives in sK[t % 3], V_t in
+    // sV[t % 3], and tiles are fetched two steps ahead of their use.
+    // Separate arrays (not one indexed at run time) let the compiler see that
+    // the DMA into one buffer never aliases reads of another.
     __shared__ __attribute__((aligned(16))) __bf16 sK0[BN * D];
     __shared__ __attribute__((aligned(16))) __bf16 sK1[BN * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sK2[BN * D];
     __shared__ __attribute__((aligned(16))) __bf16 sV0[BN * D];
     __shared__ __attribute__((aligned(16))) __bf16 sV1[BN * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sV2[BN * D];
+    // vmcnt value that leaves exactly one step's DMA (K and V) in flight
+    constexpr int kWaitOlderDma = wait_vmcnt(2 * PER);
+    static_assert(3 * PER < 64, "DMA counts must fit the 6-bit vmcnt field");
 
     // K layout in LDS: unpadded rows of DCH 16-byte chunks; chunk q of row r
     // sits at position q ^ k_swz(r).  An operand read (16 lanes = 16
@@ -134,47 +151,21 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // swizzle puts those 16 chunks in 16 distinct bank groups.
     auto v_swz = [](int key) { return DCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); };
 
-    int bh, qt;
-    tile_coords(n_bh, n_qt, CAUSAL, bh, qt);
+    // Workgroup -> (head, query tiles).  Causal: one workgroup runs query
+    // tile n_qt-1-r and then tile r, so every workgroup visits the same
+    // number of key tiles and the grid finishes in one round.
+    int bh, qt_first, qt_second;
+    tile_pair_coords(n_bh, n_qt, CAUSAL, bh, qt_first, qt_second);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int c = lane & 31;
     const int off = Skv - Sq;
-    const int q0w = qt * BM + wave * 32;
-    const int qi = q0w + c;
 
     const __bf16* Qh = Q + (size_t)bh * Sq * D;
     const __bf16* Kh = K + (size_t)bh * Skv * D;
     const __bf16* Vh = V + (size_t)bh * Skv * D;
-
-    // Q^T operand: lane holds q[qi][16 ks + 8 h .. +7]; rows past Sq read 0
-    bf16x8 qop[KS];
-    {
-        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Qh, (uint32_t)Sq * ROWB);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 x = buffer_load16(rq, (uint32_t)qi * ROWB + 32 * ks + 16 * h);
-            qop[ks] = __builtin_bit_cast(bf16x8, x);
-        }
-        // Retire the Q loads here, on every path: vmcnt is in-order, and Q
-        // loads still in flight at the loop entry would make every tile wait
-        // for its own K/V loads before the first MFMA.
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    }
-
-    float m = -INFINITY;     // running max of scale*log2(e)*s
-    float l = 0.f;           // this lane's part of the normaliser
-    f32x16 acc[ND];
-#pragma unroll
-    for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
-
-    const int q_last = min(Sq, (qt + 1) * BM) - 1;
-    const int kv_end = kv_limit(q_last, Sq, Skv, CAUSAL);
-    const int n_tiles = (kv_end + BN - 1) / BN;
-    // last key this lane's query may see (for the masked tiles)
-    const int lim = CAUSAL ? min(Skv - 1, qi + off) : Skv - 1;
 
     // ---- K/V staging: HBM -> LDS by DMA ----
     // One descriptor per head; the tile offset rides in the per-lane offset so
@@ -206,6 +197,38 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                 (uint32_t)(kv0 + key) * ROWB + 16 * chunk, 0, 0, 0);
         }
     };
+
+    // ---- one query tile: Q operand, online softmax over its key tiles, O/LSE ----
+    auto run_tile = [&](int qt) {
+    const int q0w = qt * BM + wave * 32;
+    const int qi = q0w + c;
+
+    // Q^T operand: lane holds q[qi][16 ks + 8 h .. +7]; rows past Sq read 0
+    bf16x8 qop[KS];
+    {
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Qh, (uint32_t)Sq * ROWB);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 x = buffer_load16(rq, (uint32_t)qi * ROWB + 32 * ks + 16 * h);
+            qop[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+        // Retire the Q loads here, on every path: vmcnt is in-order, and Q
+        // loads still in flight at the loop entry would make every tile wait
+        // for its own K/V loads before the first MFMA.
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+
+    float m = -INFINITY;     // running reference, scale*log2(e) units
+    float l = 0.f;           // this lane's part of the normaliser
+    f32x16 acc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
+
+    const int q_last = min(Sq, (qt + 1) * BM) - 1;
+    const int kv_end = kv_limit(q_last, Sq, Skv, CAUSAL);
+    const int n_tiles = (kv_end + BN - 1) / BN;
+    // last key this lane's query may see (for the masked tiles)
+    const int lim = CAUSAL ? min(Skv - 1, qi + off) : Skv - 1;
 
     // ---- operand reads ----
     // phase-A MFMA t: key block kb = t % NKB, k-step ks = t / NKB (the two
@@ -287,17 +310,24 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                 m = grow ? mt : m;
                 m_ref = (m == -INFINITY) ? 0.f : m;     // 0 while the row has seen no key
                 rescale = __any(grow);
+                pin(alpha);
+                pin(m_ref);
             }
             if (t >= 2) {
                 // exponentials of values [e0, e1), packed to bf16 in groups of 8
                 const int e0 = (t - 2) * NV / (NA - 2), e1 = (t - 1) * NV / (NA - 2);
 #pragma unroll
                 for (int e = e0; e < e1; ++e) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(st[e / 16][e % 16], sl2, -m_ref));
+                    float pv = __builtin_amdgcn_exp2f(fmaf(st[e / 16][e % 16], sl2, -m_ref));
+                    pin(pv);
                     v8[e & 7] = pv;
                     psum += pv;
-                    if ((e & 7) == 7) pb[e / 16][(e / 8) & 1] = __builtin_convertvector(v8, bf16x8);
+                    if ((e & 7) == 7) {
+                        pb[e / 16][(e / 8) & 1] = __builtin_convertvector(v8, bf16x8);
+                        pin(pb[e / 16][(e / 8) & 1]);
+                    }
                 }
+                pin(psum);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -327,17 +357,17 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     };
 
     using std::integral_constant;
-    // Steady-state step j.  The four buffers arrive as distinct restrict
-    // pointers: once inlined, every LDS access and DMA in the step carries
-    // scoped no-alias metadata, which lets the compiler see that the DMA into
-    // the free buffers never overlaps the operand reads of the busy ones (the
+    // Steady-state step j.  The buffers arrive as distinct restrict pointers:
+    // once inlined, every LDS access and DMA in the step carries scoped
+    // no-alias metadata, which lets the compiler see that the DMA into the
+    // free buffers never overlaps the operand reads of the busy ones (the
     // transposing read otherwise waits for all DMA in flight).
     auto step = [&](int j, f32x16* st, const __bf16* __restrict__ k_next,
                     __bf16* __restrict__ k_free, const __bf16* __restrict__ v_cur,
                     __bf16* __restrict__ v_free) {
         const int kv0 = j * BN;
-        load_k(kv0 + 2 * BN, k_free);           // K_{j+2}: zero rows or unused past the end
-        load_v(kv0 + BN, v_free);               // V_{j+1}
+        load_k(kv0 + 3 * BN, k_free);           // K_{j+3}: zero rows or unused past the end
+        load_v(kv0 + 2 * BN, v_free);           // V_{j+2}
         mask(kv0, st);
         f32x16 sn[NKB];
         bf16x8 pb[NKB][2];
@@ -346,26 +376,31 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         phase_b(v_cur, pb, alpha, rescale);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) st[kb] = sn[kb];
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // K_{j+2}, V_{j+1} have landed
+        __builtin_amdgcn_s_waitcnt(kWaitOlderDma);   // K_{j+2}, V_{j+1} have landed
         __syncthreads();
     };
-    auto last = [&](auto P, int j, f32x16* st) {
-        constexpr int p = decltype(P)::value;
+    auto last = [&](int j, f32x16* st) {
         mask(j * BN, st);
         bf16x8 pb[NKB][2];
         bool rescale;
         const float alpha =
             phase_a(integral_constant<bool, false>{}, nullptr, st, nullptr, pb, rescale);
-        phase_b(p ? sV1 : sV0, pb, alpha, rescale);
+        switch (j % 3) {
+            case 0: phase_b(sV0, pb, alpha, rescale); break;
+            case 1: phase_b(sV1, pb, alpha, rescale); break;
+            default: phase_b(sV2, pb, alpha, rescale); break;
+        }
     };
 
     if (n_tiles > 0) {
-        // ---- prologue: S_0 from K_0; K_1 and V_0 into LDS ----
+        // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0 from K_0 ----
         load_k(0, sK0);
         load_v(0, sV0);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);      // K_0 and V_0 have landed
-        __syncthreads();
         load_k(BN, sK1);
+        load_v(BN, sV1);
+        load_k(2 * BN, sK2);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * PER));   // K_0 and V_0 have landed
+        __syncthreads();
         f32x16 st[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -375,24 +410,29 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                 st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(sK0, ks * NKB + kb),
                                                                  qop[ks], st[kb], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER));   // K_1 has landed
         __syncthreads();
 
-        // ---- steady state: tiles 0 .. n_tiles - 2, two per trip ----
+        // ---- steady state: tiles 0 .. n_tiles - 2, three per trip ----
+        // buffers of step j: K_{j+1}, free slot of K_j, V_j, free slot of V_{j-1}
         int j = 0;
-        for (; j + 2 < n_tiles; j += 2) {
-            step(j, st, sK1, sK0, sV0, sV1);
-            step(j + 1, st, sK0, sK1, sV1, sV0);
+        for (; j + 3 < n_tiles; j += 3) {
+            step(j, st, sK1, sK0, sV0, sV2);
+            step(j + 1, st, sK2, sK1, sV1, sV0);
+            step(j + 2, st, sK0, sK2, sV2, sV1);
         }
-        if (j + 1 < n_tiles) {
-            step(j, st, sK1, sK0, sV0, sV1);
+        if (j + 1 < n_tiles) {                   // j % 3 == 0 here
+            step(j, st, sK1, sK0, sV0, sV2);
             ++j;
         }
-        // ---- last tile (index j = n_tiles - 1) ----
-        if (j & 1)
-            last(integral_constant<int, 1>{}, j, st);
-        else
-            last(integral_constant<int, 0>{}, j, st);
+        if (j + 1 < n_tiles) {
+            step(j, st, sK2, sK1, sV1, sV0);
+            ++j;
+        }
+        // ---- last tile (index n_tiles - 1) ----
+        last(j, st);
+        // nothing may still be landing in LDS when the next query tile starts
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
     // ---- epilogue: O = a / l, LSE = ln 2 * (m + log2 l) ----
@@ -417,6 +457,13 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         if (LSE != nullptr && h == 0)
             LSE[(size_t)bh * Sq + qi] = lt > 0.f ? (m + log2f(lt)) * kLn2f : -INFINITY;
     }
+    };
+
+    run_tile(qt_first);
+    if (qt_second >= 0) {
+        __syncthreads();      // the LDS buffers are reused by the second tile
+        run_tile(qt_second);
+    }
 }
 
 template <int D, int BN, int WAVES, bool OUT_F32>
@@ -424,7 +471,7 @@ hipError_t launch_one(const Problem& p) {
     constexpr int BM = 32 * WAVES;
     const int n_bh = p.B * p.H;
     const int n_qt = (p.Sq + BM - 1) / BM;
-    const dim3 grid((unsigned)(n_bh * n_qt));
+    const dim3 grid((unsigned)(n_bh * tile_pair_count(n_qt, p.causal)));
     const dim3 block(64 * WAVES);
     const float sl2 = p.scale * kLog2ef;
     const __bf16* q = static_cast<const __bf16*>(p.q);
@@ -441,6 +488,9 @@ hipError_t launch_one(const Problem& p) {
 
 template <int D, bool OUT_F32>
 hipError_t by_tiles(const Problem& p, int bm, int bn) {
+    if constexpr (D == 128) {
+        if (bm == 256 && bn == 32) return launch_one<D, 32, 8, OUT_F32>(p);
+    }
     if (bm == 128 && bn == 64) return launch_one<D, 64, 4, OUT_F32>(p);
     if (bm == 128 && bn == 32) return launch_one<D, 32, 4, OUT_F32>(p);
     if (bm == 64 && bn == 64) return launch_one<D, 64, 2, OUT_F32>(p);
@@ -451,12 +501,13 @@ hipError_t by_tiles(const Problem& p, int bm, int bn) {
 }  // namespace
 
 bool bf16_tiles_supported(int d, int block_m, int block_n) {
-    return (d == 64 || d == 128) && (block_m == 64 || block_m == 128) &&
-           (block_n == 32 || block_n == 64);
+    if (!(d == 64 || d == 128)) return false;
+    if (block_m == 256) return d == 128 && block_n == 32;
+    return (block_m == 64 || block_m == 128) && (block_n == 32 || block_n == 64);
 }
 
 int bf16_lds_bytes(int d, int /*block_m*/, int block_n) {
-    return 2 * 2 * block_n * d * 2;   // K and V, two buffers each
+    return 3 * 2 * block_n * d * 2;   // K and V, three buffers each
 }
 
 hipError_t launch_bf16(const Problem& p, const Tiles& t) {

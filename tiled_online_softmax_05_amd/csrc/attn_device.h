@@ -32,6 +32,28 @@ __device__ __forceinline__ void tile_coords(int n_bh, int n_qt, bool causal, int
     qt = causal ? (n_qt - 1 - rank) : rank;
 }
 
+// Pairing of query tiles for causal attention: workgroup rank r runs the
+// heavy tile n_qt-1-r and then the light tile r (second = -1 when the two
+// coincide), so all workgroups carry equal work.  Non-causal workgroups run
+// one tile each.  Consecutive ids walk the (batch, head) pairs as in
+// tile_coords, with the same XCD placement.
+__host__ __device__ __forceinline__ int tile_pair_count(int n_qt, bool causal) {
+    return causal ? (n_qt + 1) / 2 : n_qt;
+}
+__device__ __forceinline__ void tile_pair_coords(int n_bh, int n_qt, bool causal, int& bh,
+                                                 int& first, int& second) {
+    const int idx = blockIdx.x;
+    const int rank = idx / n_bh;
+    bh = idx - rank * n_bh;
+    if (causal) {
+        first = n_qt - 1 - rank;
+        second = rank < first ? rank : -1;
+    } else {
+        first = rank;
+        second = -1;
+    }
+}
+
 // Key range [0, kv_end) a workgroup of query rows [q_first, q_last] visits:
 // causal rows see keys j <= i + (Skv - Sq).
 __device__ __forceinline__ int kv_limit(int q_last, int Sq, int Skv, bool causal) {
