@@ -142,6 +142,21 @@ def test_bf16_ragged_tiles(d, causal, tiles):
                what=f"bf16->f32 300x333 d={d}")
 
 
+@pytest.mark.parametrize("tiles", [(128, 32), (64, 64), (256, 32)], ids=["128x32", "64x64", "256x32"])
+def test_bf16_every_tile_count(tiles):
+    # key lengths giving 1 .. 7 key tiles, full and ragged, so that every
+    # entry and exit of the pipelined tile loop runs (no next tile, one, two,
+    # three-step trips with each remainder)
+    d = 128
+    bn = tiles[1]
+    for n in range(1, 8):
+        for skv in sorted({(n - 1) * bn + 1, n * bn}):
+            q, k, v = random_tensors(1, 2, 70, skv, d, "bf16", "normal", seed=1000 + skv)
+            log(f"bf16 tile count {n} Skv={skv} tiles={tiles}")
+            for causal in (False, True):
+                check_full(q, k, v, causal, tiles=tiles, what=f"bf16 70x{skv} {tiles}")
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp32_ragged_all_tiles(d, causal):

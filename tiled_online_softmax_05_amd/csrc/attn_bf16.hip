@@ -272,36 +272,58 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         }
     };
 
-    // Phase A for scores st (tile j) with the next tile's K in sk: returns
-    // the accumulator rescale factor (and whether any lane of the wave needs
-    // it); fills sn (scores of tile j + 1) when NEXT and the bf16
-    // probabilities pb, and updates m and l.
-    auto phase_a = [&](auto NEXT, const __bf16* sk, const f32x16* st, f32x16* sn,
-                       bf16x8 (*pb)[2], bool& rescale) -> float {
-        constexpr bool next = decltype(NEXT)::value;
-        bf16x8 ka[3];
-        if constexpr (next) {
+    // One step of the skewed pipeline.  While the VALU turns the scores st
+    // of tile j into probabilities pn (and moves m and l), the matrix cores
+    // compute the scores sn of tile j + 1 from K in sk (when QK) and add
+    // P_{j-1} V_{j-1} (probabilities po, V in sv) to the accumulator (when
+    // PV).  Score and P.V MFMAs alternate, so each has softmax work to hide
+    // under it.  The accumulator is moved to the new reference only after
+    // the P.V MFMAs, and only when some row of the wave raised it.
+    auto fused = [&](auto QK, auto PV, const __bf16* __restrict__ sk,
+                     const __bf16* __restrict__ sv, const f32x16* st, f32x16* sn,
+                     const bf16x8 (*po)[2], bf16x8 (*pn)[2]) {
+        constexpr bool qk = decltype(QK)::value;
+        constexpr bool pv = decltype(PV)::value;
+        constexpr int NM = (qk ? NA : 0) + (pv ? NB : 0);   // MFMAs of the step
+        constexpr int NS = NM > 4 ? NM : 4;                  // schedule slots
+        bf16x8 ka[3], va[3];
+        if constexpr (qk) {
             ka[0] = k_operand(sk, 0);
             ka[1] = k_operand(sk, 1);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
         }
+        if constexpr (pv) {
+            va[0] = v_operand(sv, 0);
+            va[1] = v_operand(sv, 1);
+        }
         float mx = -INFINITY, m_ref = 0.f, alpha = 1.f, psum = 0.f;
+        bool rescale = false;
         f32x8 v8;
 #pragma unroll
-        for (int t = 0; t < NA; ++t) {
-            if constexpr (next) {
+        for (int s = 0; s < NS; ++s) {
+            // MFMA of slot s: alternate score / P.V when both run
+            const bool is_qk = qk && (!pv || (s & 1) == 0);
+            const int t = (qk && pv) ? s / 2 : s;
+            if (s >= NM) {
+                // no MFMA in this slot
+            } else if (is_qk) {
                 if (t + 2 < NA) ka[(t + 2) % 3] = k_operand(sk, t + 2);
                 const int kb = t % NKB, ks = t / NKB;
                 sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qop[ks], sn[kb], 0, 0, 0);
+            } else {
+                if (t + 2 < NB) va[(t + 2) % 3] = v_operand(sv, t + 2);
+                const int u = t / ND, i = t % ND;
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], po[u / 2][u % 2],
+                                                                 acc[i], 0, 0, 0);
             }
-            if (t == 0) {
+            if (s == 0) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
             }
-            if (t == 1) {
+            if (s == 1) {
                 mx = other_half_max(mx);
                 const float mt = mx * sl2;              // tile max, scaled base-2 domain
                 const bool grow = mt > m + kSlack;      // true on the first visible tile
@@ -313,18 +335,18 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                 pin(alpha);
                 pin(m_ref);
             }
-            if (t >= 2) {
+            if (s >= 2) {
                 // exponentials of values [e0, e1), packed to bf16 in groups of 8
-                const int e0 = (t - 2) * NV / (NA - 2), e1 = (t - 1) * NV / (NA - 2);
+                const int e0 = (s - 2) * NV / (NS - 2), e1 = (s - 1) * NV / (NS - 2);
 #pragma unroll
                 for (int e = e0; e < e1; ++e) {
-                    float pv = __builtin_amdgcn_exp2f(fmaf(st[e / 16][e % 16], sl2, -m_ref));
-                    pin(pv);
-                    v8[e & 7] = pv;
-                    psum += pv;
+                    float pv_ = __builtin_amdgcn_exp2f(fmaf(st[e / 16][e % 16], sl2, -m_ref));
+                    pin(pv_);
+                    v8[e & 7] = pv_;
+                    psum += pv_;
                     if ((e & 7) == 7) {
-                        pb[e / 16][(e / 8) & 1] = __builtin_convertvector(v8, bf16x8);
-                        pin(pb[e / 16][(e / 8) & 1]);
+                        pn[e / 16][(e / 8) & 1] = __builtin_convertvector(v8, bf16x8);
+                        pin(pn[e / 16][(e / 8) & 1]);
                     }
                 }
                 pin(psum);
@@ -332,74 +354,67 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             __builtin_amdgcn_sched_barrier(0);
         }
         l = l * alpha + psum;
-        return alpha;
-    };
-
-    // Phase B: rescale the accumulator if the reference moved, then
-    // O^T += V^T P^T from sv.
-    auto phase_b = [&](const __bf16* __restrict__ sv, const bf16x8 (*pb)[2], float alpha,
-                       bool rescale) {
+        // acc holds sum_{t <= j-1} relative to the old reference; move it to
+        // the new one before P_j V_j is added in the next step
         if (rescale) {
 #pragma unroll
             for (int i = 0; i < ND; ++i) acc[i] *= alpha;
         }
+    };
+
+    using std::integral_constant;
+    using T_ = integral_constant<bool, true>;
+    using F_ = integral_constant<bool, false>;
+    // P.V of the last tile: acc += P V from sv.
+    auto pv_tile = [&](const __bf16* sv, const bf16x8 (*p)[2]) {
         bf16x8 va[3];
         va[0] = v_operand(sv, 0);
         va[1] = v_operand(sv, 1);
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
-            const int s = t / ND, i = t % ND;
             if (t + 2 < NB) va[(t + 2) % 3] = v_operand(sv, t + 2);
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], pb[s / 2][s % 2], acc[i],
+            const int u = t / ND, i = t % ND;
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], p[u / 2][u % 2], acc[i],
                                                              0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     using std::integral_constant;
-    // Steady-state step j.  The buffers arrive as distinct restrict pointers:
-    // once inlined, every LDS access and DMA in the step carries scoped
-    // no-alias metadata, which lets the compiler see that the DMA into the
-    // free buffers never overlaps the operand reads of the busy ones (the
-    // transposing read otherwise waits for all DMA in flight).
-    auto step = [&](int j, f32x16* st, const __bf16* __restrict__ k_next,
-                    __bf16* __restrict__ k_free, const __bf16* __restrict__ v_cur,
-                    __bf16* __restrict__ v_free) {
+    using T_ = integral_constant<bool, true>;
+    using F_ = integral_constant<bool, false>;
+    // Steady-state step j: scores of tile j + 1, P.V of tile j - 1, softmax
+    // of tile j; DMA of K_{j+3} and V_{j+1}.  The buffers arrive as distinct
+    // restrict pointers: once inlined, every LDS access and DMA in the step
+    // carries scoped no-alias metadata, which lets the compiler see that the
+    // DMA into the free buffers never overlaps the operand reads of the busy
+    // ones (the transposing read otherwise waits for all DMA in flight).
+    auto step = [&](auto PV, int j, f32x16* st, bf16x8 (*po)[2],
+                    const __bf16* __restrict__ k_next, __bf16* __restrict__ k_free,
+                    const __bf16* __restrict__ v_prev, __bf16* __restrict__ v_free) {
         const int kv0 = j * BN;
         load_k(kv0 + 3 * BN, k_free);           // K_{j+3}: zero rows or unused past the end
-        load_v(kv0 + 2 * BN, v_free);           // V_{j+2}
+        load_v(kv0 + BN, v_free);               // V_{j+1}
         mask(kv0, st);
         f32x16 sn[NKB];
-        bf16x8 pb[NKB][2];
-        bool rescale;
-        const float alpha = phase_a(integral_constant<bool, true>{}, k_next, st, sn, pb, rescale);
-        phase_b(v_cur, pb, alpha, rescale);
+        bf16x8 pn[NKB][2];
+        fused(T_{}, PV, k_next, v_prev, st, sn, po, pn);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) st[kb] = sn[kb];
-        __builtin_amdgcn_s_waitcnt(kWaitOlderDma);   // K_{j+2}, V_{j+1} have landed
-        __syncthreads();
-    };
-    auto last = [&](int j, f32x16* st) {
-        mask(j * BN, st);
-        bf16x8 pb[NKB][2];
-        bool rescale;
-        const float alpha =
-            phase_a(integral_constant<bool, false>{}, nullptr, st, nullptr, pb, rescale);
-        switch (j % 3) {
-            case 0: phase_b(sV0, pb, alpha, rescale); break;
-            case 1: phase_b(sV1, pb, alpha, rescale); break;
-            default: phase_b(sV2, pb, alpha, rescale); break;
+        for (int kb = 0; kb < NKB; ++kb) {
+            st[kb] = sn[kb];
+            po[kb][0] = pn[kb][0];
+            po[kb][1] = pn[kb][1];
         }
+        __builtin_amdgcn_s_waitcnt(kWaitOlderDma);   // K_{j+2}, V_j have landed
+        __syncthreads();
     };
 
     if (n_tiles > 0) {
-        // ---- prologue: K_0, V_0, K_1, V_1, K_2 in flight; S_0 from K_0 ----
+        // ---- prologue: K_0, K_1, V_0, K_2 in flight; S_0 from K_0 ----
         load_k(0, sK0);
-        load_v(0, sV0);
         load_k(BN, sK1);
-        load_v(BN, sV1);
+        load_v(0, sV0);
         load_k(2 * BN, sK2);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * PER));   // K_0 and V_0 have landed
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * PER));   // K_0 has landed
         __syncthreads();
         f32x16 st[NKB];
 #pragma unroll
@@ -413,26 +428,42 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER));   // K_1 has landed
         __syncthreads();
 
-        // ---- steady state: tiles 0 .. n_tiles - 2, three per trip ----
-        // buffers of step j: K_{j+1}, free slot of K_j, V_j, free slot of V_{j-1}
+        // ---- steps 0 .. n_tiles - 2 (each has a next tile) ----
+        // buffers of step j: K_{j+1}, free slot of K_j, V_{j-1}, free slot of V_{j-2}
+        bf16x8 po[NKB][2];      // probabilities of the previous tile
         int j = 0;
-        for (; j + 3 < n_tiles; j += 3) {
-            step(j, st, sK1, sK0, sV0, sV2);
-            step(j + 1, st, sK2, sK1, sV1, sV0);
-            step(j + 2, st, sK0, sK2, sV2, sV1);
+        if (n_tiles > 1) {
+            step(F_{}, 0, st, po, sK1, sK0, sV2, sV1);     // no P.V yet
+            j = 1;
+            for (; j + 3 < n_tiles; j += 3) {
+                step(T_{}, j, st, po, sK2, sK1, sV0, sV2);
+                step(T_{}, j + 1, st, po, sK0, sK2, sV1, sV0);
+                step(T_{}, j + 2, st, po, sK1, sK0, sV2, sV1);
+            }
+            if (j + 1 < n_tiles) {               // j % 3 == 1 here
+                step(T_{}, j, st, po, sK2, sK1, sV0, sV2);
+                ++j;
+            }
+            if (j + 1 < n_tiles) {
+                step(T_{}, j, st, po, sK0, sK2, sV1, sV0);
+                ++j;
+            }
         }
-        if (j + 1 < n_tiles) {                   // j % 3 == 0 here
-            step(j, st, sK1, sK0, sV0, sV2);
-            ++j;
-        }
-        if (j + 1 < n_tiles) {
-            step(j, st, sK2, sK1, sV1, sV0);
-            ++j;
-        }
-        // ---- last tile (index n_tiles - 1) ----
-        last(j, st);
-        // nothing may still be landing in LDS when the next query tile starts
+        // ---- last tile j = n_tiles - 1: P.V of tile j - 1, softmax of
+        // tile j, then its P.V.  All DMA has landed first (also what the
+        // next query tile needs).
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        const int r = j % 3;
+        const __bf16* v_prev = r == 0 ? sV2 : (r == 1 ? sV0 : sV1);
+        const __bf16* v_last = r == 0 ? sV0 : (r == 1 ? sV1 : sV2);
+        mask(j * BN, st);
+        bf16x8 pn[NKB][2];
+        if (j > 0)
+            fused(F_{}, T_{}, nullptr, v_prev, st, nullptr, po, pn);
+        else
+            fused(F_{}, F_{}, nullptr, nullptr, st, nullptr, po, pn);
+        pv_tile(v_last, pn);
     }
 
     // ---- epilogue: O = a / l, LSE = ln 2 * (m + log2 l) ----
