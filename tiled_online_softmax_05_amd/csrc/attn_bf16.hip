@@ -70,6 +70,40 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
+// The same descriptor as four words, for the DMA below.
+__device__ __forceinline__ i32x4 buffer_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int32_t)(uint32_t)a, (int32_t)((a >> 32) & 0xFFFF), (int32_t)bytes,
+                 kBufferFlags};
+}
+
+// HBM -> LDS DMA of 16 bytes per lane (buffer_load ... lds): lane l's bytes
+// land at LDS byte address lds + 16 l, offsets past the descriptor's range
+// read 0.  Written as inline asm so that the compiler does not track it as
+// an LDS write: the kernel orders every DMA against the LDS reads itself
+// (explicit vmcnt waits and barriers around the ring of buffers), while the
+// compiler's tracking cannot tell the ring's buffers apart across steps and
+// would wait for prefetches that no read depends on.  Hidden from the
+// compiler's counters, these loads can only make its own vmcnt waits for
+// ordinary loads stricter.  M0 must be written one instruction before the
+// DMA that reads it.
+// M0 is a reserved register: clang warns that clobbering it is not
+// preserved across the statement, which is what is meant here (the compiler
+// sets M0 itself before each of its own uses).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds, uint32_t voffset) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 
 // Empty register-level barrier: makes x an output of a volatile statement at
 // this point, so IR passes cannot sink the code producing x past it (the
@@ -77,6 +111,17 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 template <typename T>
 __device__ __forceinline__ void pin(T& x) {
     asm volatile("" : "+v"(x));
+}
+
+// Workgroup barrier for the LDS ring.  __syncthreads() also fences memory
+// at workgroup scope, and the compiler implements that release by waiting
+// for every load in flight -- including the DMA just issued for tiles two
+// steps ahead, which would cut the prefetch depth to one step.  Here the
+// caller first waits (s_waitcnt) for exactly the DMA the next step reads;
+// LDS operand reads have been consumed by then; the memory clobber keeps the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float other_half_max(float x) {
@@ -168,33 +213,35 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const __bf16* Vh = V + (size_t)bh * Skv * D;
 
     // ---- K/V staging: HBM -> LDS by DMA ----
-    // One descriptor per head; the tile offset rides in the per-lane offset so
-    // rows at or past Skv fall outside the descriptor's range and read 0.
     // Slot S = i * NT + tid (16 bytes) of LDS row S / DCH holds chunk
-    // (S % DCH) ^ swizzle(row) of that row's key.
-    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(Kh, (uint32_t)Skv * ROWB);
-    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(Vh, (uint32_t)Skv * ROWB);
+    // (S % DCH) ^ swizzle(row) of that row's key.  Each tile gets a
+    // descriptor over rows [kv0, Skv) of the head (empty from Skv on), so
+    // rows at or past Skv fall outside its range and read 0; the tile offset
+    // moves the base on the scalar unit and each lane's offset within a tile
+    // is fixed for the whole kernel.
+    auto tile_words = [&](const __bf16* head, int kv0) {
+        const int k0 = min(kv0, Skv);
+        return buffer_words(head + (size_t)k0 * D, (uint32_t)(Skv - k0) * ROWB);
+    };
     auto load_k = [&](int kv0, __bf16* dst) {
+        const i32x4 r = tile_words(Kh, kv0);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int S = i * NT + tid;
             const int row = S / DCH;
             const int chunk = (S % DCH) ^ k_swz(row);
             const int key = (row & ~31) + sigma(row & 31);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, (__attribute__((address_space(3))) void*)(dst + (i * NT + wave * 64) * 8), 16,
-                (uint32_t)(kv0 + key) * ROWB + 16 * chunk, 0, 0, 0);
+            dma16(r, lds_addr(dst + (i * NT + wave * 64) * 8), (uint32_t)key * ROWB + 16 * chunk);
         }
     };
     auto load_v = [&](int kv0, __bf16* dst) {
+        const i32x4 r = tile_words(Vh, kv0);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int S = i * NT + tid;
             const int key = S / DCH;
             const int chunk = (S % DCH) ^ v_swz(key);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, (__attribute__((address_space(3))) void*)(dst + (i * NT + wave * 64) * 8), 16,
-                (uint32_t)(kv0 + key) * ROWB + 16 * chunk, 0, 0, 0);
+            dma16(r, lds_addr(dst + (i * NT + wave * 64) * 8), (uint32_t)key * ROWB + 16 * chunk);
         }
     };
 
@@ -214,7 +261,10 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         }
         // Retire the Q loads here, on every path: vmcnt is in-order, and Q
         // loads still in flight at the loop entry would make every tile wait
-        // for its own K/V loads before the first MFMA.
+        // for its own K/V loads before the first MFMA.  (The empty asm uses
+        // the registers, so the loads cannot sink below this point.)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) pin(qop[ks]);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
@@ -299,7 +349,24 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         }
         float mx = -INFINITY, m_ref = 0.f, alpha = 1.f, psum = 0.f;
         bool rescale = false;
-        f32x8 v8;
+        float ex[NV];
+        // row sum of values [p0, p1), packed to bf16 in groups of 8
+        auto sum_pack = [&](int p0, int p1) {
+#pragma unroll
+            for (int e = p0; e < p1; ++e) {
+                psum += ex[e];
+                if ((e & 7) == 7) {
+                    const int b = e - 7;
+                    bf16x8& pk = pn[e / 16][(e / 8) & 1];
+                    pk = __builtin_convertvector(
+                        (f32x8){ex[b], ex[b + 1], ex[b + 2], ex[b + 3], ex[b + 4], ex[b + 5],
+                                ex[b + 6], ex[b + 7]},
+                        bf16x8);
+                    pin(pk);
+                }
+            }
+            pin(psum);
+        };
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             // MFMA of slot s: alternate score / P.V when both run
@@ -336,23 +403,20 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                 pin(m_ref);
             }
             if (s >= 2) {
-                // exponentials of values [e0, e1), packed to bf16 in groups of 8
+                // exponentials of values [e0, e1) of this slot; the row sum
+                // and the bf16 packing of the previous slot's values, so that
+                // no add reads an exponential issued just before it
                 const int e0 = (s - 2) * NV / (NS - 2), e1 = (s - 1) * NV / (NS - 2);
 #pragma unroll
                 for (int e = e0; e < e1; ++e) {
-                    float pv_ = __builtin_amdgcn_exp2f(fmaf(st[e / 16][e % 16], sl2, -m_ref));
-                    pin(pv_);
-                    v8[e & 7] = pv_;
-                    psum += pv_;
-                    if ((e & 7) == 7) {
-                        pn[e / 16][(e / 8) & 1] = __builtin_convertvector(v8, bf16x8);
-                        pin(pn[e / 16][(e / 8) & 1]);
-                    }
+                    ex[e] = __builtin_amdgcn_exp2f(fmaf(st[e / 16][e % 16], sl2, -m_ref));
+                    pin(ex[e]);
                 }
-                pin(psum);
+                if (s >= 3) sum_pack((s - 3) * NV / (NS - 2), e0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        sum_pack((NS - 3) * NV / (NS - 2), NV);     // the last slot's values
         l = l * alpha + psum;
         // acc holds sum_{t <= j-1} relative to the old reference; move it to
         // the new one before P_j V_j is added in the next step
@@ -405,7 +469,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             po[kb][1] = pn[kb][1];
         }
         __builtin_amdgcn_s_waitcnt(kWaitOlderDma);   // K_{j+2}, V_j have landed
-        __syncthreads();
+        ring_barrier();
     };
 
     if (n_tiles > 0) {
@@ -415,7 +479,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         load_v(0, sV0);
         load_k(2 * BN, sK2);
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * PER));   // K_0 has landed
-        __syncthreads();
+        ring_barrier();
         f32x16 st[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -426,7 +490,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                                                                  qop[ks], st[kb], 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER));   // K_1 has landed
-        __syncthreads();
+        ring_barrier();
 
         // ---- steps 0 .. n_tiles - 2 (each has a next tile) ----
         // buffers of step j: K_{j+1}, free slot of K_j, V_{j-1}, free slot of V_{j-2}

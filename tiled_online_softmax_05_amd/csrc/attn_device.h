@@ -16,6 +16,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // Workgroup order.  Workgroups are numbered so that consecutive ids walk
 // over the (batch, head) pairs of one query-tile rank.  With causal masking
