@@ -115,6 +115,57 @@ int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* 
 int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal,
                       int* block_m, int* block_n, int* waves, int* lds_bytes);
 
+/*
+ * attn_fwd_split -- attn_fwd with the key range cut into chunks that run in
+ * separate workgroups, for problems whose query tiles alone leave compute
+ * units idle (few heads, short query blocks against long key sequences, as
+ * in decoding against a cached prefix).  Each chunk c produces the partial
+ * state of the online normalisation of "Tiled attention: preserving results
+ * without a full score matrix" (section "Online normalization") over its own
+ * keys -- O_c = a_c / l_c and LSE_c = m_c + ln l_c -- and a second kernel
+ * merges the states of each row with the same rescale rule applied to whole
+ * states: M = max_c LSE_c, w_c = exp(LSE_c - M),
+ *     O = sum_c w_c O_c / sum_c w_c,   LSE = M + ln sum_c w_c.
+ * Results equal attn_fwd's up to rounding (not bitwise).
+ *
+ *   q ... stream  : as attn_fwd (tiles from attn_select_tiles).
+ *   n_splits      : number of key chunks; 0 = choose (attn_select_splits).
+ *                   Rounded to whole key tiles, so fewer chunks may run; 1
+ *                   runs attn_fwd's path.  At most 4096.
+ *   workspace     : caller-owned device buffer, 256-byte aligned, of at least
+ *                   attn_split_workspace_bytes(B, H, Sq, d, n) bytes for the
+ *                   number of chunks that runs (for n_splits = 0, ask
+ *                   attn_select_splits).  It must not overlap q, k, v, o or
+ *                   lse.  May be NULL when one chunk runs.  Its contents are
+ *                   scratch: overwritten, never read before written.
+ *   workspace_bytes : its size.
+ * Returns as attn_fwd; ATTN_ERR_INVALID_ARG also for a missing or too small
+ * workspace, ATTN_ERR_MISALIGNED for a workspace not 256-byte aligned.
+ * Enqueues two kernels on `stream` when the key range is split.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Sq, int Skv, int d, float scale, int causal,
+                   int dtype, void* stream, int n_splits, void* workspace,
+                   long long workspace_bytes);
+
+/*
+ * attn_select_splits -- the key-chunk count attn_fwd_split uses for
+ * n_splits = 0 (host only, no HIP call): 1 when the query tiles alone give
+ * every compute unit a workgroup, else enough chunks of whole key tiles to
+ * do so (at most 64).  Writes the count and the chunk length in keys; either
+ * pointer may be NULL.  Returns as attn_select_tiles.
+ */
+int attn_select_splits(int d, int Sq, int Skv, int BH, int dtype, int causal,
+                       int* n_splits, int* kv_chunk);
+
+/*
+ * attn_split_workspace_bytes -- bytes of workspace attn_fwd_split needs for
+ * n_splits key chunks: partial O [n_splits, B, H, Sq, d] fp32, then at a
+ * 256-byte boundary partial LSE [n_splits, B, H, Sq] fp64.  Returns -1 for
+ * invalid sizes (negative, d <= 0, n_splits outside [1, 4096]).
+ */
+long long attn_split_workspace_bytes(int B, int H, int Sq, int d, int n_splits);
+
 /* attn_last_error -- message for the last non-OK status on this thread
  * ("" if none).  The string stays valid until the next call on the thread. */
 const char* attn_last_error(void);

@@ -31,12 +31,13 @@ def kind(t: torch.Tensor) -> str:
 
 
 def gpu_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
-            scale: Optional[float] = None, out_dtype=None, tiles=None
+            scale: Optional[float] = None, out_dtype=None, tiles=None, splits=None
             ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Copy host inputs to cuda:0, run attn_fwd, return device O and LSE."""
+    """Copy host inputs to cuda:0, run attn_fwd (attn_fwd_split when
+    ``splits`` is an int), return device O and LSE."""
     dev = torch.device("cuda", 0)
     o, lse = binding.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale,
-                         out_dtype=out_dtype, tiles=tiles)
+                         out_dtype=out_dtype, tiles=tiles, splits=splits)
     torch.cuda.synchronize()
     return o, lse
 
@@ -82,9 +83,10 @@ def oracle_full(q, k, v, causal: bool, scale: Optional[float] = None):
     return oracle.direct_attention(to_f64(q), to_f64(k), to_f64(v), scale=scale, causal=causal)
 
 
-def check_full(q, k, v, causal: bool, scale=None, out_dtype=None, tiles=None, what=""):
+def check_full(q, k, v, causal: bool, scale=None, out_dtype=None, tiles=None, what="",
+               splits=None):
     """Whole-output parity at the strict tolerance of the input dtype."""
-    o, lse = gpu_run(q, k, v, causal, scale, out_dtype, tiles)
+    o, lse = gpu_run(q, k, v, causal, scale, out_dtype, tiles, splits)
     o_ref, lse_ref = oracle_full(q, k, v, causal, scale)
     compare(o, lse, o_ref, lse_ref, O_TOL[kind(q)], LSE_TOL[kind(q)], what)
     return o, lse, o_ref, lse_ref

@@ -16,7 +16,8 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:long\s+long|\w+)\**\s+\**(attn_\w+)\s*\(",
+                                 text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert lib.attn_version() == 100
+    assert lib.attn_version() == 101
 
 
 @pytest.mark.parametrize("args,want", [
@@ -126,3 +127,60 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 32)
     with pytest.raises(ValueError):
         B.fwd(q, q, q)
+
+
+# ------------------------------------------------------------------ attn_fwd_split (host side)
+def test_split_workspace_bytes(lib):
+    # partial O (fp32) rounded up to 256 bytes, then partial LSE (fp64)
+    rows = 3 * 2 * 8
+    for n in (1, 2, 7):
+        want = (n * rows * 32 * 4 + 255) // 256 * 256 + n * rows * 8
+        assert B.split_workspace_bytes(3, 2, 8, 32, n) == want
+    for bad in ((3, 2, 8, 32, 0), (3, 2, 8, 0, 2), (-1, 2, 8, 32, 2), (3, 2, 8, 32, 5000)):
+        with pytest.raises(B.AttnError):
+            B.split_workspace_bytes(*bad)
+
+
+@pytest.mark.parametrize("args,split", [
+    # (d, Sq, Skv, BH, dtype, causal): the stress workloads fill the GPU only when split
+    ((32, 8, 1000, 6, B.F32, 0), True),
+    ((32, 8, 257, 6, B.F32, 1), True),
+    ((32, 8, 64, 6, B.F32, 1), False),            # one key tile: nothing to split
+    ((128, 1, 4000, 8, B.BF16, 0), True),
+    ((128, 4096, 4096, 32, B.BF16, 1), False),     # enough query tiles already
+    ((64, 100, 0, 8, B.BF16, 0), False),           # no keys
+])
+def test_select_splits(lib, args, split):
+    n, chunk = B.select_splits(*args)
+    d, Sq, Skv, BH, dtype, causal = args
+    _, bn, _, _ = B.select_tiles(*args)
+    assert (n > 1) == split
+    assert 1 <= n <= 64
+    if Skv:
+        assert chunk % bn == 0 and (n - 1) * chunk < Skv <= n * chunk
+
+
+def _split(lib, n_splits=2, ws=0x600000, ws_bytes=1 << 20, **kw):
+    base = dict(q=A0, k=A1, v=A2, o=A3, lse=A4, Bn=1, H=2, Sq=64, Skv=64, d=64, scale=0.125,
+                causal=0, dtype=B.F32)
+    base.update(kw)
+    return lib.attn_fwd_split(base["q"], base["k"], base["v"], base["o"], base["lse"], base["Bn"],
+                              base["H"], base["Sq"], base["Skv"], base["d"], base["scale"],
+                              base["causal"], base["dtype"], None, n_splits, ws, ws_bytes)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_splits=-1), B.ERR_INVALID_ARG),
+    (dict(n_splits=5000), B.ERR_INVALID_ARG),
+    (dict(ws=None), B.ERR_INVALID_ARG),                       # chunks need a workspace
+    (dict(ws_bytes=64), B.ERR_INVALID_ARG),                   # too small
+    (dict(ws=0x600000 + 16), B.ERR_MISALIGNED),
+    (dict(ws=A3), B.ERR_INVALID_ARG),                         # overlaps o
+    (dict(ws=A0), B.ERR_INVALID_ARG),                         # overlaps q
+    (dict(causal=2), B.ERR_INVALID_ARG),
+    (dict(d=48), B.ERR_UNSUPPORTED),
+    (dict(n_splits=0, ws=None, Sq=8, Skv=1000, d=32), B.ERR_INVALID_ARG),  # auto split, no workspace
+])
+def test_split_invalid_arguments_rejected_on_host(lib, kw, status):
+    assert _split(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""

@@ -27,7 +27,8 @@ STATUS_NAMES = {OK: "ATTN_OK", ERR_INVALID_ARG: "ATTN_ERR_INVALID_ARG",
                 ERR_UNSUPPORTED: "ATTN_ERR_UNSUPPORTED", ERR_MISALIGNED: "ATTN_ERR_MISALIGNED",
                 ERR_HIP: "ATTN_ERR_HIP"}
 
-EXPORTED = ("attn_fwd", "attn_fwd_tiles", "attn_select_tiles", "attn_last_error",
+EXPORTED = ("attn_fwd", "attn_fwd_tiles", "attn_select_tiles", "attn_fwd_split",
+            "attn_select_splits", "attn_split_workspace_bytes", "attn_last_error",
             "attn_version")
 
 
@@ -60,6 +61,13 @@ def load() -> ctypes.CDLL:
         pi = ctypes.POINTER(ctypes.c_int)
         lib.attn_select_tiles.argtypes = [ip, ip, ip, ip, ip, ip, pi, pi, pi, pi]
         lib.attn_select_tiles.restype = ip
+        ll = ctypes.c_longlong
+        lib.attn_fwd_split.argtypes = fwd_args + [ip, vp, ll]
+        lib.attn_fwd_split.restype = ip
+        lib.attn_select_splits.argtypes = [ip, ip, ip, ip, ip, ip, pi, pi]
+        lib.attn_select_splits.restype = ip
+        lib.attn_split_workspace_bytes.argtypes = [ip, ip, ip, ip, ip]
+        lib.attn_split_workspace_bytes.restype = ll
         lib.attn_last_error.argtypes = []
         lib.attn_last_error.restype = ctypes.c_char_p
         lib.attn_version.argtypes = []
@@ -84,6 +92,24 @@ def select_tiles(d: int, Sq: int, Skv: int, BH: int, dtype: int, causal: bool
     out = [ctypes.c_int(0) for _ in range(4)]
     check(lib.attn_select_tiles(d, Sq, Skv, BH, dtype, int(causal), *[ctypes.byref(x) for x in out]))
     return tuple(x.value for x in out)
+
+
+def select_splits(d: int, Sq: int, Skv: int, BH: int, dtype: int, causal: bool
+                  ) -> Tuple[int, int]:
+    """The library's key-chunk choice for attn_fwd_split: (n_splits, kv_chunk)."""
+    lib = load()
+    n, chunk = ctypes.c_int(0), ctypes.c_int(0)
+    check(lib.attn_select_splits(d, Sq, Skv, BH, dtype, int(causal), ctypes.byref(n),
+                                 ctypes.byref(chunk)))
+    return n.value, chunk.value
+
+
+def split_workspace_bytes(B: int, H: int, Sq: int, d: int, n_splits: int) -> int:
+    """Workspace bytes attn_fwd_split needs for n_splits key chunks."""
+    r = load().attn_split_workspace_bytes(B, H, Sq, d, n_splits)
+    if r < 0:
+        raise AttnError(ERR_INVALID_ARG, last_error())
+    return int(r)
 
 
 def _dtype_code(t: torch.dtype, out_dtype: Optional[torch.dtype]) -> int:
@@ -114,17 +140,30 @@ def fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: Optional[in
         check(lib.attn_fwd_tiles(*args, int(tiles[0]), int(tiles[1])))
 
 
+def fwd_split_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: Optional[int],
+                  B: int, H: int, Sq: int, Skv: int, d: int, scale: float, causal: bool,
+                  dtype: int, stream: int, n_splits: int, ws_ptr: Optional[int],
+                  ws_bytes: int) -> None:
+    """Direct call of ``attn_fwd_split`` on raw device pointers."""
+    check(load().attn_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Sq, Skv, d,
+                                float(scale), int(causal), dtype, stream, int(n_splits),
+                                ws_ptr, int(ws_bytes)))
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
         tiles: Optional[Tuple[int, int]] = None, with_lse: bool = True,
-        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        splits: Optional[int] = None
         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """O, LSE = attention(q, k, v) on the GPU through ``attn_fwd``.
 
     ``q`` is ``[B, H, Sq, d]``, ``k`` and ``v`` ``[B, H, Skv, d]``, contiguous
     CUDA(HIP) tensors of one dtype (float32 or bfloat16).  ``scale`` defaults to
-    ``1/sqrt(d)``.  ``tiles=(block_m, block_n)`` forces a tile shape.  The call
-    is enqueued on torch's current stream of q's device."""
+    ``1/sqrt(d)``.  ``tiles=(block_m, block_n)`` forces a tile shape.
+    ``splits`` (an int, 0 = the library's choice) calls ``attn_fwd_split``
+    instead, with a workspace allocated here.  The call is enqueued on torch's
+    current stream of q's device."""
     lib = load()
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors (there is no CPU path)")
@@ -149,8 +188,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    lse_ptr = lse.data_ptr() if lse is not None else None
     with torch.cuda.device(q.device):
-        fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                lse.data_ptr() if lse is not None else None, B, H, Sq, Skv, d, scale, causal,
-                code, stream, tiles)
+        if splits is None:
+            fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, H, Sq,
+                    Skv, d, scale, causal, code, stream, tiles)
+        else:
+            if tiles is not None:
+                raise ValueError("tiles and splits cannot be combined")
+            n = int(splits) if splits > 0 else select_splits(d, Sq, Skv, B * H, code, causal)[0]
+            nbytes = split_workspace_bytes(B, H, Sq, d, max(n, 1))
+            ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
+            base = (ws.data_ptr() + 255) // 256 * 256
+            fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B,
+                          H, Sq, Skv, d, scale, causal, code, stream, n, base, nbytes)
     return out, lse

@@ -45,6 +45,47 @@ __global__ void empty_rows_kernel(void* __restrict__ o, int o_bytes, float* __re
             lse[i] = -INFINITY;
 }
 
+// Merge of the key chunks' partial states.  Chunk c of a query row holds
+// O_c = a_c / l_c and LSE_c = m_c + ln l_c (-inf when the chunk saw no key
+// of the row).  The online normalisation's rescale rule applied to whole
+// states gives, with M = max_c LSE_c and w_c = exp(LSE_c - M),
+//     O = sum_c w_c O_c / sum_c w_c,   LSE = M + ln sum_c w_c,
+// and O = 0, LSE = -inf when no chunk saw a key.  One thread per (row, four
+// channels); weights and sums in fp64.
+__global__ void merge_kernel(const float* __restrict__ part_o,
+                             const double* __restrict__ part_lse, void* __restrict__ o,
+                             int o_bytes, float* __restrict__ lse, size_t rows, int d,
+                             int n_splits) {
+    const int d4 = d / 4;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * d4) return;
+    const size_t row = idx / d4;
+    const int ch = 4 * (int)(idx - row * d4);
+    double M = -INFINITY;
+    for (int c = 0; c < n_splits; ++c) M = fmax(M, part_lse[c * rows + row]);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    double W = 0.0;
+    if (M != -INFINITY) {
+        for (int c = 0; c < n_splits; ++c) {
+            const double lc = part_lse[c * rows + row];
+            if (lc == -INFINITY) continue;
+            const double w = exp(lc - M);
+            W += w;
+            const float* oc = part_o + (c * rows + row) * d + ch;
+            for (int r = 0; r < 4; ++r) acc[r] += w * (double)oc[r];
+        }
+    }
+    const double inv = W > 0.0 ? 1.0 / W : 0.0;
+    if (o_bytes == 4) {
+        float* out = static_cast<float*>(o) + row * d + ch;
+        for (int r = 0; r < 4; ++r) out[r] = (float)(acc[r] * inv);
+    } else {
+        __bf16* out = static_cast<__bf16*>(o) + row * d + ch;
+        for (int r = 0; r < 4; ++r) out[r] = (__bf16)(float)(acc[r] * inv);
+    }
+    if (lse != nullptr && ch == 0) lse[row] = W > 0.0 ? (float)(M + log(W)) : -INFINITY;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -93,6 +134,31 @@ int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
     return ATTN_OK;
 }
 
+// Workspace of attn_fwd_split: partial O [n, B*H, Sq, d] fp32, then (at a
+// 256-byte boundary) partial LSE [n, B*H, Sq] fp64.
+int64_t part_o_bytes(int64_t rows, int d, int n) { return (n * rows * d * 4 + 255) / 256 * 256; }
+int64_t split_workspace(int64_t rows, int d, int n) { return part_o_bytes(rows, d, n) + n * rows * 8; }
+
+// Key chunks for attn_fwd_split.  Without a split the grid has `items`
+// workgroups; when that leaves CUs idle, the key range is cut into chunks
+// of whole key tiles so that items x chunks covers the CUs (at most 64
+// chunks).  `want` = 0 asks for that choice; otherwise the caller's count,
+// rounded to whole tiles.  Returns the chunk count and length.
+void split_plan(const Tiles& t, int Sq, int Skv, int BH, int dtype, bool causal, int want,
+                int* n_splits, int* kv_chunk) {
+    constexpr long kCUs = 256;
+    const long n_qt = (Sq + t.block_m - 1) / t.block_m;
+    const long items = (long)BH * (dtype == ATTN_F32 ? n_qt : (causal ? (n_qt + 1) / 2 : n_qt));
+    long n = want;
+    if (n <= 0) n = items >= kCUs ? 1 : std::min<long>(64, (kCUs + items - 1) / std::max(items, 1L));
+    n = std::max<long>(1, std::min<long>(n, (Skv + t.block_n - 1) / t.block_n));
+    long chunk = (Skv + n - 1) / n;
+    chunk = (chunk + t.block_n - 1) / t.block_n * t.block_n;
+    *kv_chunk = (int)std::max<long>(chunk, t.block_n);
+    *n_splits = (int)((Skv + *kv_chunk - 1) / *kv_chunk);
+    if (*n_splits < 1) *n_splits = 1;
+}
+
 int validate(const Problem& p) {
     if (p.dtype != ATTN_F32 && p.dtype != ATTN_BF16 && p.dtype != ATTN_BF16_OUT_F32)
         return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", p.dtype);
@@ -134,10 +200,30 @@ int validate(const Problem& p) {
     return ATTN_OK;
 }
 
-int run(const Problem& p, int block_m, int block_n) {
+// want_splits < 0: no split (attn_fwd); >= 0: attn_fwd_split with the
+// caller's workspace.
+int run(const Problem& p_in, int block_m, int block_n, int want_splits = -1,
+        void* workspace = nullptr, int64_t workspace_bytes = 0) {
+    Problem p = p_in;
     int st = validate(p);
     if (st != ATTN_OK) return st;
     const int bh = p.B * p.H;
+    if (want_splits >= 0) {
+        const int64_t need = split_workspace((int64_t)bh * p.Sq, p.d, std::max(want_splits, 1));
+        if (want_splits > 0 && (workspace == nullptr || workspace_bytes < need))
+            return fail(ATTN_ERR_INVALID_ARG, "workspace of %lld bytes too small (need %lld)",
+                        (long long)workspace_bytes, (long long)need);
+        if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return fail(ATTN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+        const size_t ib = (size_t)in_bytes(p.dtype);
+        const size_t nq = (size_t)bh * p.Sq * p.d, nkv = (size_t)bh * p.Skv * p.d;
+        const size_t wb = (size_t)std::max<int64_t>(workspace_bytes, 0);
+        if (overlaps(workspace, wb, p.q, nq * ib) || overlaps(workspace, wb, p.k, nkv * ib) ||
+            overlaps(workspace, wb, p.v, nkv * ib) ||
+            overlaps(workspace, wb, p.o, nq * out_bytes(p.dtype)) ||
+            overlaps(workspace, wb, p.lse, (size_t)bh * p.Sq * 4))
+            return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps an input or an output");
+    }
     if (bh == 0 || p.Sq == 0) return ok();
     Tiles t{};
     if (block_m == 0 && block_n == 0) {
@@ -159,10 +245,24 @@ int run(const Problem& p, int block_m, int block_n) {
         hipLaunchKernelGGL(empty_rows_kernel, dim3(blocks), dim3(256), 0, p.stream, p.o,
                            out_bytes(p.dtype), p.lse, elems, (size_t)bh * p.Sq);
         e = hipGetLastError();
-    } else if (p.dtype == ATTN_F32) {
-        e = launch_f32(p, t);
     } else {
-        e = launch_bf16(p, t);
+        int n = 1, chunk = p.Skv;
+        if (want_splits >= 0)
+            split_plan(t, p.Sq, p.Skv, bh, p.dtype, p.causal, want_splits, &n, &chunk);
+        if (n > 1) {
+            const int64_t rows = (int64_t)bh * p.Sq;
+            const int64_t need = split_workspace(rows, p.d, n);
+            if (workspace == nullptr || workspace_bytes < need)
+                return fail(ATTN_ERR_INVALID_ARG, "workspace of %lld bytes too small (need %lld)",
+                            (long long)workspace_bytes, (long long)need);
+            p.n_splits = n;
+            p.kv_chunk = chunk;
+            p.part_o = static_cast<float*>(workspace);
+            p.part_lse = reinterpret_cast<double*>(static_cast<char*>(workspace) +
+                                                   part_o_bytes(rows, p.d, n));
+        }
+        e = p.dtype == ATTN_F32 ? launch_f32(p, t) : launch_bf16(p, t);
+        if (e == hipSuccess && n > 1) e = launch_merge(p);
     }
     if (e != hipSuccess)
         return fail(ATTN_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -170,6 +270,16 @@ int run(const Problem& p, int block_m, int block_n) {
 }
 
 }  // namespace
+
+hipError_t launch_merge(const Problem& p) {
+    const size_t rows = (size_t)p.B * p.H * p.Sq;
+    const size_t threads = rows * (p.d / 4);
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(256), 0, p.stream, p.part_o,
+                       p.part_lse, p.o, out_bytes(p.dtype), p.lse, rows, p.d, p.n_splits);
+    return hipGetLastError();
+}
+
 }  // namespace attn
 
 extern "C" {
@@ -209,8 +319,43 @@ int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal, int
     return attn::ok();
 }
 
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int Sq, int Skv, int d, float scale, int causal, int dtype,
+                   void* stream, int n_splits, void* workspace, long long workspace_bytes) {
+    if (causal != 0 && causal != 1)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+    if (n_splits < 0 || n_splits > 4096)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "n_splits must be in [0, 4096] (got %d)",
+                          n_splits);
+    attn::Problem p{q, k, v, o, lse, B, H, Sq, Skv, d, scale, causal == 1, dtype,
+                    static_cast<hipStream_t>(stream)};
+    return attn::run(p, 0, 0, n_splits, workspace, workspace_bytes);
+}
+
+int attn_select_splits(int d, int Sq, int Skv, int BH, int dtype, int causal, int* n_splits,
+                       int* kv_chunk) {
+    int bm = 0, bn = 0, waves = 0, lds = 0;
+    const int st = attn_select_tiles(d, Sq, Skv, BH, dtype, causal, &bm, &bn, &waves, &lds);
+    if (st != ATTN_OK) return st;
+    attn::Tiles t{bm, bn, waves, lds};
+    int n = 1, chunk = Skv;
+    if (Skv > 0) attn::split_plan(t, Sq, Skv, BH, dtype, causal == 1, 0, &n, &chunk);
+    if (n_splits) *n_splits = n;
+    if (kv_chunk) *kv_chunk = chunk;
+    return attn::ok();
+}
+
+long long attn_split_workspace_bytes(int B, int H, int Sq, int d, int n_splits) {
+    if (B < 0 || H < 0 || Sq < 0 || d <= 0 || n_splits < 1 || n_splits > 4096) {
+        attn::fail(ATTN_ERR_INVALID_ARG, "invalid size for the split workspace");
+        return -1;
+    }
+    attn::ok();
+    return (long long)attn::split_workspace((int64_t)B * H * Sq, d, n_splits);
+}
+
 const char* attn_last_error(void) { return attn::g_last_error.c_str(); }
 
-int attn_version(void) { return 100; }
+int attn_version(void) { return 101; }
 
 }  // extern "C"

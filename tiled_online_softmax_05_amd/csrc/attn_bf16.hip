@@ -154,7 +154,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                           const __bf16* __restrict__ V, void* __restrict__ Out,
                           float* __restrict__ LSE, int n_bh, int Sq, int Skv, float sl2,
-                          int n_qt) {
+                          int n_qt, int kv_chunk, float* __restrict__ part_o,
+                          double* __restrict__ part_lse) {
     constexpr int BM = 32 * WAVES;
     constexpr int NT = 64 * WAVES;
     constexpr int KS = D / 16;         // k-steps of the score contraction
@@ -274,9 +275,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 #pragma unroll
     for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
 
+    // key chunk blockIdx.y of the (possibly split) key range
     const int q_last = min(Sq, (qt + 1) * BM) - 1;
-    const int kv_end = kv_limit(q_last, Sq, Skv, CAUSAL);
-    const int n_tiles = (kv_end + BN - 1) / BN;
+    const int kv_begin = (int)blockIdx.y * kv_chunk;
+    const int kv_end = min(kv_limit(q_last, Sq, Skv, CAUSAL), kv_begin + min(kv_chunk, Skv));
+    const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BN - 1) / BN : 0;
     // last key this lane's query may see (for the masked tiles)
     const int lim = CAUSAL ? min(Skv - 1, qi + off) : Skv - 1;
 
@@ -455,7 +458,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     auto step = [&](auto PV, int j, f32x16* st, bf16x8 (*po)[2],
                     const __bf16* __restrict__ k_next, __bf16* __restrict__ k_free,
                     const __bf16* __restrict__ v_prev, __bf16* __restrict__ v_free) {
-        const int kv0 = j * BN;
+        const int kv0 = kv_begin + j * BN;
         load_k(kv0 + 3 * BN, k_free);           // K_{j+3}: zero rows or unused past the end
         load_v(kv0 + BN, v_free);               // V_{j+1}
         mask(kv0, st);
@@ -474,10 +477,10 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
     if (n_tiles > 0) {
         // ---- prologue: K_0, K_1, V_0, K_2 in flight; S_0 from K_0 ----
-        load_k(0, sK0);
-        load_k(BN, sK1);
-        load_v(0, sV0);
-        load_k(2 * BN, sK2);
+        load_k(kv_begin, sK0);
+        load_k(kv_begin + BN, sK1);
+        load_v(kv_begin, sV0);
+        load_k(kv_begin + 2 * BN, sK2);
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * PER));   // K_0 has landed
         ring_barrier();
         f32x16 st[NKB];
@@ -521,7 +524,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         const int r = j % 3;
         const __bf16* v_prev = r == 0 ? sV2 : (r == 1 ? sV0 : sV1);
         const __bf16* v_last = r == 0 ? sV0 : (r == 1 ? sV1 : sV2);
-        mask(j * BN, st);
+        mask(kv_begin + j * BN, st);
         bf16x8 pn[NKB][2];
         if (j > 0)
             fused(F_{}, T_{}, nullptr, v_prev, st, nullptr, po, pn);
@@ -534,23 +537,41 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const float lt = other_half_sum(l);
     if (qi < Sq) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const size_t obase = ((size_t)bh * Sq + qi) * D;
+        const size_t row = (size_t)bh * Sq + qi;
+        if (part_o != nullptr) {
+            // partial state of this key chunk: O_c = a_c / l_c, LSE_c in fp64
+            const size_t prow = (size_t)blockIdx.y * n_bh * Sq + row;
 #pragma unroll
-        for (int i = 0; i < ND; ++i)
+            for (int i = 0; i < ND; ++i)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int ch = 32 * i + 8 * r4 + 4 * h;
-                f32x4 o4 = {acc[i][4 * r4 + 0] * inv, acc[i][4 * r4 + 1] * inv,
-                            acc[i][4 * r4 + 2] * inv, acc[i][4 * r4 + 3] * inv};
-                if constexpr (OUT_F32) {
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(Out) + obase + ch) = o4;
-                } else {
-                    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + obase + ch) =
-                        __builtin_convertvector(o4, bf16x4);
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int ch = 32 * i + 8 * r4 + 4 * h;
+                    const f32x4 o4 = {acc[i][4 * r4 + 0] * inv, acc[i][4 * r4 + 1] * inv,
+                                      acc[i][4 * r4 + 2] * inv, acc[i][4 * r4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(part_o + prow * D + ch) = o4;
                 }
-            }
-        if (LSE != nullptr && h == 0)
-            LSE[(size_t)bh * Sq + qi] = lt > 0.f ? (m + log2f(lt)) * kLn2f : -INFINITY;
+            if (h == 0)
+                part_lse[prow] =
+                    lt > 0.f ? ((double)m + log2((double)lt)) * (double)kLn2f : -INFINITY;
+        } else {
+            const size_t obase = row * D;
+#pragma unroll
+            for (int i = 0; i < ND; ++i)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int ch = 32 * i + 8 * r4 + 4 * h;
+                    f32x4 o4 = {acc[i][4 * r4 + 0] * inv, acc[i][4 * r4 + 1] * inv,
+                                acc[i][4 * r4 + 2] * inv, acc[i][4 * r4 + 3] * inv};
+                    if constexpr (OUT_F32) {
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(Out) + obase + ch) = o4;
+                    } else {
+                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + obase + ch) =
+                            __builtin_convertvector(o4, bf16x4);
+                    }
+                }
+            if (LSE != nullptr && h == 0)
+                LSE[row] = lt > 0.f ? (m + log2f(lt)) * kLn2f : -INFINITY;
+        }
     }
     };
 
@@ -566,7 +587,7 @@ hipError_t launch_one(const Problem& p) {
     constexpr int BM = 32 * WAVES;
     const int n_bh = p.B * p.H;
     const int n_qt = (p.Sq + BM - 1) / BM;
-    const dim3 grid((unsigned)(n_bh * tile_pair_count(n_qt, p.causal)));
+    const dim3 grid((unsigned)(n_bh * tile_pair_count(n_qt, p.causal)), (unsigned)p.n_splits);
     const dim3 block(64 * WAVES);
     const float sl2 = p.scale * kLog2ef;
     const __bf16* q = static_cast<const __bf16*>(p.q);
@@ -574,10 +595,12 @@ hipError_t launch_one(const Problem& p) {
     const __bf16* v = static_cast<const __bf16*>(p.v);
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, WAVES, true, OUT_F32>), grid, block, 0,
-                           p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt);
+                           p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt,
+                           p.kv_chunk, p.part_o, p.part_lse);
     else
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, WAVES, false, OUT_F32>), grid, block, 0,
-                           p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt);
+                           p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt,
+                           p.kv_chunk, p.part_o, p.part_lse);
     return hipGetLastError();
 }
 

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(64 * WAVES)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, float* __restrict__ O,
                          float* __restrict__ LSE, int n_bh, int Sq, int Skv, double scale,
-                         int n_qt) {
+                         int n_qt, int kv_chunk, float* __restrict__ part_o,
+                         double* __restrict__ part_lse) {
     constexpr int BM = 16 * WAVES;
     constexpr int NT = 64 * WAVES;
     constexpr int DQ = D / 4;      // head-dim quarter per lane group
@@ -86,10 +87,12 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < ND; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // key chunk blockIdx.y of the (possibly split) key range
     const int q_last = min(Sq, (qt + 1) * BM) - 1;
-    const int kv_end = kv_limit(q_last, Sq, Skv, CAUSAL);
+    const int kv_begin = (int)blockIdx.y * kv_chunk;
+    const int kv_end = min(kv_limit(q_last, Sq, Skv, CAUSAL), kv_begin + min(kv_chunk, Skv));
 
-    for (int kv0 = 0; kv0 < kv_end; kv0 += BN) {
+    for (int kv0 = kv_begin; kv0 < kv_end; kv0 += BN) {
         __syncthreads();
         for (int e = tid; e < BN * (D / 4); e += NT) {
             const int row = e / (D / 4);
@@ -172,12 +175,23 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     lt += __shfl_xor(lt, 32);
     if (qi < Sq) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        float* orow = O + ((size_t)bh * Sq + qi) * D + 4 * g;
+        const double lse = lt > 0.f ? m + log((double)lt) : -INFINITY;
+        const size_t row = (size_t)bh * Sq + qi;
+        if (part_o == nullptr) {
+            float* orow = O + row * D + 4 * g;
 #pragma unroll
-        for (int i = 0; i < ND; ++i)
-            *reinterpret_cast<f32x4*>(orow + 16 * i) = acc[i] * inv;
-        if (LSE != nullptr && g == 0)
-            LSE[(size_t)bh * Sq + qi] = lt > 0.f ? (float)(m + log((double)lt)) : -INFINITY;
+            for (int i = 0; i < ND; ++i)
+                *reinterpret_cast<f32x4*>(orow + 16 * i) = acc[i] * inv;
+            if (LSE != nullptr && g == 0) LSE[row] = (float)lse;
+        } else {
+            // partial state of this key chunk: O_c = a_c / l_c, LSE_c in fp64
+            const size_t prow = (size_t)blockIdx.y * n_bh * Sq + row;
+            float* orow = part_o + prow * D + 4 * g;
+#pragma unroll
+            for (int i = 0; i < ND; ++i)
+                *reinterpret_cast<f32x4*>(orow + 16 * i) = acc[i] * inv;
+            if (g == 0) part_lse[prow] = lse;
+        }
     }
 }
 
@@ -186,7 +200,7 @@ hipError_t launch_one(const Problem& p) {
     constexpr int BM = 16 * WAVES;
     const int n_bh = p.B * p.H;
     const int n_qt = (p.Sq + BM - 1) / BM;
-    const dim3 grid((unsigned)(n_bh * n_qt));
+    const dim3 grid((unsigned)(n_bh * n_qt), (unsigned)p.n_splits);
     const dim3 block(64 * WAVES);
     const double scale = (double)p.scale;
     const float* q = static_cast<const float*>(p.q);
@@ -195,10 +209,12 @@ hipError_t launch_one(const Problem& p) {
     float* o = static_cast<float*>(p.o);
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, true>), grid, block, 0, p.stream,
-                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt);
+                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.kv_chunk,
+                           p.part_o, p.part_lse);
     else
         hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, false>), grid, block, 0, p.stream,
-                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt);
+                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.kv_chunk,
+                           p.part_o, p.part_lse);
     return hipGetLastError();
 }
 

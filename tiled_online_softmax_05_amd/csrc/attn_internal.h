@@ -19,6 +19,15 @@ struct Problem {
     bool causal;
     int dtype;           // attn_dtype
     hipStream_t stream;
+    // Split of the key range (attn_fwd_split): key chunk c = blockIdx.y
+    // covers keys [c * kv_chunk, (c + 1) * kv_chunk).  With part_o set, the
+    // kernels write each chunk's partial state -- O_c = a_c / l_c (fp32) and
+    // LSE_c (fp64) -- to [n_splits, B*H, Sq, d] and [n_splits, B*H, Sq]
+    // instead of o and lse, and launch_merge() combines them.
+    int n_splits = 1;
+    int kv_chunk = 0x7FFFFFFF;
+    float* part_o = nullptr;
+    double* part_lse = nullptr;
 };
 
 // Tile shape chosen by the selector or forced by the caller.
@@ -35,6 +44,8 @@ hipError_t launch_f32(const Problem& p, const Tiles& t);
 hipError_t launch_bf16(const Problem& p, const Tiles& t);
 // Fill O with zeros and LSE with -inf (Skv == 0: no row sees a key).
 hipError_t launch_empty_rows(const Problem& p);
+// Combine the n_splits partial states in part_o / part_lse into o and lse.
+hipError_t launch_merge(const Problem& p);
 
 // Tile shapes that have a kernel, and their LDS footprint.
 bool f32_tiles_supported(int d, int block_m, int block_n);
