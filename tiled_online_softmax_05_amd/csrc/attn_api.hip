@@ -2,6 +2,7 @@
 // and dispatch to the gfx950 kernels.  See include/attn.h for the contract.
 #include "attn.h"
 #include "attn_internal.h"
+#include "attn_device.h"
 
 #include <algorithm>
 #include <cmath>
@@ -51,7 +52,13 @@ __global__ void empty_rows_kernel(void* __restrict__ o, int o_bytes, float* __re
 // states gives, with M = max_c LSE_c and w_c = exp(LSE_c - M),
 //     O = sum_c w_c O_c / sum_c w_c,   LSE = M + ln sum_c w_c,
 // and O = 0, LSE = -inf when no chunk saw a key.  One thread per (row, four
-// channels); weights and sums in fp64.
+// channels) runs over the chunks in batches of kMergeBatch, all of a batch's
+// loads in flight together, keeping a running maximum M and rescaling its
+// running sums by exp(M_old - M_new) when a batch raises it (the same rule
+// once more).  Differences LSE_c - M are taken in fp64 (LSE reaches
+// hundreds), their exponentials (<= 1) in fp32, the sums in fp64.
+constexpr int kMergeBatch = 8;
+
 __global__ void merge_kernel(const float* __restrict__ part_o,
                              const double* __restrict__ part_lse, void* __restrict__ o,
                              int o_bytes, float* __restrict__ lse, size_t rows, int d,
@@ -61,27 +68,48 @@ __global__ void merge_kernel(const float* __restrict__ part_o,
     if (idx >= rows * d4) return;
     const size_t row = idx / d4;
     const int ch = 4 * (int)(idx - row * d4);
-    double M = -INFINITY;
-    for (int c = 0; c < n_splits; ++c) M = fmax(M, part_lse[c * rows + row]);
+    double M = -INFINITY, W = 0.0;
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    double W = 0.0;
-    if (M != -INFINITY) {
-        for (int c = 0; c < n_splits; ++c) {
-            const double lc = part_lse[c * rows + row];
-            if (lc == -INFINITY) continue;
-            const double w = exp(lc - M);
-            W += w;
-            const float* oc = part_o + (c * rows + row) * d + ch;
-            for (int r = 0; r < 4; ++r) acc[r] += w * (double)oc[r];
+    for (int c0 = 0; c0 < n_splits; c0 += kMergeBatch) {
+        double lc[kMergeBatch];
+        f32x4 oc[kMergeBatch];
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            const int c = c0 + u;
+            lc[u] = -INFINITY;
+            oc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (c < n_splits) {
+                lc[u] = part_lse[c * rows + row];
+                oc[u] = *reinterpret_cast<const f32x4*>(part_o + (c * rows + row) * d + ch);
+            }
         }
+        double mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) mb = fmax(mb, lc[u]);
+        if (mb == -INFINITY) continue;          // no chunk of the batch saw a key of the row
+        const double mn = fmax(M, mb);
+        const double r = M == -INFINITY ? 0.0 : (double)expf((float)(M - mn));
+        W *= r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= r;
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u) {
+            if (lc[u] == -INFINITY) continue;
+            const double w = (double)expf((float)(lc[u] - mn));
+            W += w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += w * (double)oc[u][i];
+        }
+        M = mn;
     }
     const double inv = W > 0.0 ? 1.0 / W : 0.0;
     if (o_bytes == 4) {
-        float* out = static_cast<float*>(o) + row * d + ch;
-        for (int r = 0; r < 4; ++r) out[r] = (float)(acc[r] * inv);
+        const f32x4 v = {(float)(acc[0] * inv), (float)(acc[1] * inv), (float)(acc[2] * inv),
+                         (float)(acc[3] * inv)};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * d + ch) = v;
     } else {
         __bf16* out = static_cast<__bf16*>(o) + row * d + ch;
-        for (int r = 0; r < 4; ++r) out[r] = (__bf16)(float)(acc[r] * inv);
+        for (int i = 0; i < 4; ++i) out[i] = (__bf16)(float)(acc[i] * inv);
     }
     if (lse != nullptr && ch == 0) lse[row] = W > 0.0 ? (float)(M + log(W)) : -INFINITY;
 }
