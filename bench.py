@@ -116,6 +116,10 @@ def main(argv=None) -> int:
     ap.add_argument("--splits", type=int, default=None,
                     help="time attn_fwd_split with this many key chunks (0 = library choice)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--flush", action="store_true",
+                    help="overwrite a 1 GiB buffer before each timed launch (outside the "
+                         "per-launch events), so K/V start outside L2 and Infinity Cache; "
+                         "value then comes from the events")
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -179,9 +183,12 @@ def main(argv=None) -> int:
     # timed region: exactly `steps` launches, HIP events around each on the launch stream
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev) if a.flush else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
+        if scrub is not None:
+            scrub.fill_(float(i))
         starts[i].record(stream)
         step()
         ends[i].record(stream)
@@ -192,13 +199,16 @@ def main(argv=None) -> int:
     med_ms = sorted(launch_ms)[len(launch_ms) // 2]
 
     flops = attention_flops(w.B, w.H, w.Sq, w.Skv, w.d, causal)
-    ms_per_step = wall * 1e3 / a.steps
-    value = flops / (wall / a.steps) / 1e12
+    # with --flush the wall clock also holds the scrubs: use the launch events
+    ms_per_step = avg_ms if a.flush else wall * 1e3 / a.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype_name]
     in_b = 4 if dtype_name == "f32" else 2
     comp = compulsory_bytes(w.B, w.H, w.Sq, w.Skv, w.d, in_b, in_b)
-    traffic = measured_traffic(a.workload)
+    # counters were taken on the default launch (selector tiles, one key chunk, warm cache)
+    default_launch = a.tiles is None and n_splits is None and not a.flush
+    traffic = measured_traffic(a.workload) if default_launch else None
 
     # bound: MFMA above the ridge point (peak FLOP/s over HBM bytes/s), HBM below
     if flops / comp >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
@@ -224,7 +234,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": a.workload, "B": w.B, "H": w.H, "Sq": w.Sq, "Skv": w.Skv,
                    "d": w.d, "causal": causal, "tiles": list(tiles_used),
-                   "key_chunks": n_splits or 1, "input_dist": w.dist, "seed": w.seed},
+                   "key_chunks": n_splits or 1, "cache": "flushed" if a.flush else "warm",
+                   "input_dist": w.dist, "seed": w.seed},
         "roofline": roofline,
     }
     roofline.update({"launch_ms_avg": round(avg_ms, 5), "launch_ms_median": round(med_ms, 5),
