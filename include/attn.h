@@ -78,7 +78,7 @@ typedef enum {
  *   lse      : output [B, H, Sq] float32, or NULL to skip it.
  *   B, H     : batch and heads (>= 0).
  *   Sq, Skv  : query and key lengths (>= 0).  Sq == 0 is a no-op.
- *   d        : head dimension: 32, 64 or 128 (fp32); 64 or 128 (bf16).
+ *   d        : head dimension: 16, 32, 64 or 128 (fp32); 64 or 128 (bf16).
  *   scale    : score scale, finite and > 0 (usually 1/sqrt(d)).
  *   causal   : 0 or 1 (end-aligned mask above).
  *   dtype    : an attn_dtype.
@@ -97,6 +97,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * function on "Verify tiled attention").  block_m = block_n = 0 means "use
  * the selector".  Built shapes:
  *   ATTN_F32            block_m in {16, 32, 64},  block_n in {16, 32, 64}
+ *                       (every d)
  *   ATTN_BF16[_OUT_F32] block_m in {64, 128},     block_n in {32, 64},
  *                       and block_m = 256 with block_n = 32 when d = 128
  * Any other pair returns ATTN_ERR_UNSUPPORTED.

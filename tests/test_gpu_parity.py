@@ -157,7 +157,7 @@ def test_bf16_every_tile_count(tiles):
                 check_full(q, k, v, causal, tiles=tiles, what=f"bf16 70x{skv} {tiles}")
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp32_ragged_all_tiles(d, causal):
     q, k, v = random_tensors(2, 2, 77, 133, d, "f32", "normal", seed=23 + d)
@@ -257,3 +257,29 @@ def test_no_lse_pointer():
     assert lse is None
     o_ref, _ = oracle_full(q, k, v, True)
     compare(o, None, o_ref, None, O_TOL["bf16"], 0, "no LSE")
+
+
+# ------------------------------------------------------------------ the pages' pinned example on the GPU
+def test_p1_pinned_example_d16_on_gpu():
+    # "Verify tiled attention" (section "Compare the attention outputs"): the
+    # lab's seed-42 example, S = 64, d = 16, causal, scale 1/4, 16 x 16 tiles,
+    # with the printed sample rows (6 decimals) -- here on the GPU in fp32
+    from pin_checks import golden
+    from seeded_inputs import p1_make_qkv
+    g = golden("p1_lab_results.json")
+    st = g["setup"]
+    qn, kn, vn = p1_make_qkv(st["seq_len"], st["head_dim"], st["seed"])
+    q, k, v = [torch.from_numpy(x).to(torch.float32).reshape(1, 1, 64, 16) for x in (qn, kn, vn)]
+    scale = 1.0 / math.sqrt(st["head_dim"])
+    for tiles in ((st["block_q"], st["block_kv"]), None):
+        o, lse = gpu_run(q, k, v, True, scale=scale, tiles=tiles)
+        o_ref, lse_ref = oracle.direct_attention(to_f64(q), to_f64(k), to_f64(v), scale=scale,
+                                                 causal=True)
+        compare(o, lse, o_ref, lse_ref, O_TOL["f32"], LSE_TOL["f32"], f"P1 seed 42 d=16 {tiles}")
+        oc = o.cpu().double().numpy()[0, 0]
+        # row 0 sees one key: exactly V[0]
+        assert np.array_equal(o.cpu()[0, 0, 0], v[0, 0, 0])
+        # printed rows, rounded to 6 decimals, from fp64 inputs (fp32 here: ~1e-7 more)
+        pr = g["printed"]
+        assert np.max(np.abs(oc[0, :4] - pr["sample_row0_first4"])) <= 5e-7 + 1e-6
+        assert np.max(np.abs(oc[63, :4] - pr["sample_last_row_first4"])) <= 5e-7 + 1e-6

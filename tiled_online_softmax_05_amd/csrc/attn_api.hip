@@ -130,8 +130,8 @@ int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
     constexpr long kCUs = 256;
     auto wgs = [&](int bm) { return (long)BH * ((Sq + bm - 1) / bm); };
     if (dtype == ATTN_F32) {
-        if (!(d == 32 || d == 64 || d == 128))
-            return fail(ATTN_ERR_UNSUPPORTED, "fp32 head dim %d not built (32, 64, 128)", d);
+        if (!(d == 16 || d == 32 || d == 64 || d == 128))
+            return fail(ATTN_ERR_UNSUPPORTED, "fp32 head dim %d not built (16, 32, 64, 128)", d);
         int bn = Skv > 32 ? 64 : (Skv > 16 ? 32 : 16);
         int bm = 64;
         while (bm > 16 && (wgs(bm) < kCUs || Sq <= bm / 2)) bm /= 2;
@@ -194,7 +194,7 @@ int validate(const Problem& p) {
         return fail(ATTN_ERR_INVALID_ARG, "negative size (B=%d H=%d Sq=%d Skv=%d)", p.B, p.H,
                     p.Sq, p.Skv);
     if (p.d <= 0) return fail(ATTN_ERR_INVALID_ARG, "head dim %d must be positive", p.d);
-    if (p.dtype == ATTN_F32 ? !(p.d == 32 || p.d == 64 || p.d == 128)
+    if (p.dtype == ATTN_F32 ? !(p.d == 16 || p.d == 32 || p.d == 64 || p.d == 128)
                             : !(p.d == 64 || p.d == 128))
         return fail(ATTN_ERR_UNSUPPORTED, "head dim %d not built for dtype %d", p.d, p.dtype);
     if (!std::isfinite(p.scale) || !(p.scale > 0.f))

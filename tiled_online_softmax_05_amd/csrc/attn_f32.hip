@@ -241,7 +241,7 @@ hipError_t by_bn(const Problem& p, int bn, int waves) {
 }  // namespace
 
 bool f32_tiles_supported(int d, int block_m, int block_n) {
-    const bool dm = d == 32 || d == 64 || d == 128;
+    const bool dm = d == 16 || d == 32 || d == 64 || d == 128;
     const bool bm = block_m == 16 || block_m == 32 || block_m == 64;
     const bool bn = block_n == 16 || block_n == 32 || block_n == 64;
     return dm && bm && bn;
@@ -255,6 +255,7 @@ hipError_t launch_f32(const Problem& p, const Tiles& t) {
     if (!f32_tiles_supported(p.d, t.block_m, t.block_n)) return hipErrorInvalidValue;
     const int waves = t.block_m / 16;
     switch (p.d) {
+        case 16: return by_bn<16>(p, t.block_n, waves);
         case 32: return by_bn<32>(p, t.block_n, waves);
         case 64: return by_bn<64>(p, t.block_n, waves);
         case 128: return by_bn<128>(p, t.block_n, waves);
