@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s and % MFMA peak (bf16 H=32 S=4096 d=128 causal)"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "f64": 78.6}
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_h32_s4096_d128.json")
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_device.h", "attn_api.hip"]
@@ -148,8 +148,9 @@ def main(argv=None) -> int:
     odt = q.dtype
     out = torch.empty(q.shape, dtype=odt, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    code = binding.F32 if odt == torch.float32 else binding.BF16
-    dtype_name = "f32" if odt == torch.float32 else "bf16"
+    code = {torch.float32: binding.F32, torch.bfloat16: binding.BF16,
+            torch.float16: binding.F16}[odt]
+    dtype_name = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[odt]
     scale = 1.0 / math.sqrt(w.d)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream

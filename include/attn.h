@@ -55,8 +55,11 @@ typedef enum {
                               exponentials, l and P.V are fp32.              */
     ATTN_BF16 = 1,         /* q, k, v, o bfloat16; QK^T and P.V on bf16 MFMA
                               with fp32 accumulation, P rounded to bf16 (RNE). */
-    ATTN_BF16_OUT_F32 = 2  /* q, k, v bfloat16, o float32 (same arithmetic as
+    ATTN_BF16_OUT_F32 = 2, /* q, k, v bfloat16, o float32 (same arithmetic as
                               ATTN_BF16, output not rounded to bf16).         */
+    ATTN_F16 = 3,          /* q, k, v, o float16 (IEEE half); fp16 MFMA with
+                              fp32 accumulation, P rounded to fp16 (RNE).     */
+    ATTN_F16_OUT_F32 = 4   /* q, k, v float16, o float32.                     */
 } attn_dtype;
 
 typedef enum {
@@ -78,7 +81,8 @@ typedef enum {
  *   lse      : output [B, H, Sq] float32, or NULL to skip it.
  *   B, H     : batch and heads (>= 0).
  *   Sq, Skv  : query and key lengths (>= 0).  Sq == 0 is a no-op.
- *   d        : head dimension: 16, 32, 64 or 128 (fp32); 64 or 128 (bf16).
+ *   d        : head dimension: 16, 32, 64 or 128 (fp32); 64 or 128 (bf16,
+ *              fp16).
  *   scale    : score scale, finite and > 0 (usually 1/sqrt(d)).
  *   causal   : 0 or 1 (end-aligned mask above).
  *   dtype    : an attn_dtype.
@@ -98,7 +102,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * the selector".  Built shapes:
  *   ATTN_F32            block_m in {16, 32, 64},  block_n in {16, 32, 64}
  *                       (every d)
- *   ATTN_BF16[_OUT_F32] block_m in {64, 128},     block_n in {32, 64},
+ *   ATTN_BF16[_OUT_F32], ATTN_F16[_OUT_F32]
+ *                       block_m in {64, 128},     block_n in {32, 64},
  *                       and block_m = 256 with block_n = 32 when d = 128
  * Any other pair returns ATTN_ERR_UNSUPPORTED.
  */

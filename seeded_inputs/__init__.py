@@ -29,7 +29,8 @@ reference implementation, in full"):
   V uniform(-1, 1); Sq = 8 against Skv in {64, 257, 1000, 1024}, plus the
   causal Sq = Skv = 1000 case.
 
-Rounding to bf16 is torch's round-to-nearest-even ``.to(torch.bfloat16)``.
+Rounding to bf16 (or fp16, for the fp16 path) is torch's round-to-nearest-even
+``.to(torch.bfloat16)`` (``.to(torch.float16)``).
 """
 from __future__ import annotations
 
@@ -49,7 +50,7 @@ class Workload:
     Sq: int
     Skv: int
     d: int
-    dtype: str          # storage type of Q, K, V: "f32" or "bf16"
+    dtype: str          # storage type of Q, K, V: "f32", "bf16" or "f16"
     dist: str           # "uniform0.8", "normal", "stress"
     seed: int
     causal_modes: Tuple[bool, ...]
@@ -79,6 +80,10 @@ WORKLOADS: Dict[str, Workload] = {
                  303, (True,)),
         Workload("longctx_h64_s32768_d128", 1, 64, 32768, 32768, 128, "bf16", "normal",
                  404, (True,)),
+        # the S = 4096, H = 32, d = 128 prefill with fp16 storage (the other
+        # 2-byte element the byte model of "Verify tiled attention" assumes)
+        Workload("prefill_h32_s4096_d128_f16", 1, 32, 4096, 4096, 128, "f16", "uniform0.8",
+                 306, (True,)),
         _stress("stress_b3h2_d32_skv64", 8, 64, 501, (False, True)),
         _stress("stress_b3h2_d32_skv257", 8, 257, 502, (False, True)),
         _stress("stress_b3h2_d32_skv1000", 8, 1000, 503, (False, True)),
@@ -114,8 +119,9 @@ def make_tensors(w: Workload, seed: int | None = None
         v = _uniform(g, ks, -1.0, 1.0)
     else:
         raise ValueError(f"unknown distribution {w.dist!r}")
-    if w.dtype == "bf16":
-        q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    if w.dtype in ("bf16", "f16"):
+        t = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        q, k, v = q.to(t), k.to(t), v.to(t)
     elif w.dtype != "f32":
         raise ValueError(f"unknown dtype {w.dtype!r}")
     return q.contiguous(), k.contiguous(), v.contiguous()
@@ -148,5 +154,5 @@ def p1_make_qkv(seq_len: int, head_dim: int, seed: int = 42
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
-    """Exact widening of an fp32 / bf16 host tensor to a float64 numpy array."""
+    """Exact widening of an fp32 / bf16 / fp16 host tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()

@@ -15,10 +15,14 @@ from seeded_inputs import to_f64
 from tiled_online_softmax_05_amd import binding
 
 # Tolerances.  O: max-abs 1e-5 for fp32 inputs and 1e-2 for bf16 inputs.
+# fp16 (not in the stated bar; derived): P is rounded to fp16 (relative
+# 2^-11) and O is stored in fp16 (half an ulp: 2^-11 relative at |O| < 1,
+# 2^-9 at |O| < 4); with fp32 accumulation the error stays below 2e-3 for the
+# N(0,1) and U(-0.8, 0.8) inputs here.
 # LSE (not on the pages): |dLSE| <= tol * max(1, |LSE|); fp32 stores LSE with a
-# relative rounding of 6e-8 and the bf16 path's fp32 scores carry ~1e-6.
-O_TOL = {"f32": 1e-5, "bf16": 1e-2}
-LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
+# relative rounding of 6e-8 and the 16-bit paths' fp32 scores carry ~1e-6.
+O_TOL = {"f32": 1e-5, "bf16": 1e-2, "f16": 2e-3}
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-4, "f16": 1e-4}
 
 
 def log(msg: str) -> None:
@@ -27,7 +31,7 @@ def log(msg: str) -> None:
 
 
 def kind(t: torch.Tensor) -> str:
-    return "f32" if t.dtype == torch.float32 else "bf16"
+    return {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[t.dtype]
 
 
 def gpu_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,

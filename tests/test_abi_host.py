@@ -53,6 +53,8 @@ def test_version(lib):
     ((64, 4096, 4096, 32, B.BF16_OUT_F32, 0), (128, 32, 4)),
     ((128, 4096, 4096, 16, B.BF16, 1), (128, 32, 4)),
     ((128, 1024, 1024, 2, B.BF16, 1), (64, 32, 2)),
+    ((128, 4096, 4096, 32, B.F16, 1), (128, 32, 4)),
+    ((64, 4096, 4096, 32, B.F16_OUT_F32, 0), (128, 32, 4)),
 ])
 def test_selector(lib, args, want):
     bm, bn, waves, lds = B.select_tiles(*args)
@@ -93,7 +95,8 @@ def _call(lib, q=A0, k=A1, v=A2, o=A3, lse=A4, Bn=1, H=2, Sq=64, Skv=64, d=64, s
     (dict(d=0), B.ERR_INVALID_ARG),
     (dict(d=48), B.ERR_UNSUPPORTED),
     (dict(d=32, dtype=B.BF16), B.ERR_UNSUPPORTED),
-    (dict(dtype=3), B.ERR_INVALID_ARG),
+    (dict(dtype=5), B.ERR_INVALID_ARG),
+    (dict(d=32, dtype=B.F16), B.ERR_UNSUPPORTED),
     (dict(scale=float("nan")), B.ERR_INVALID_ARG),
     (dict(scale=float("inf")), B.ERR_INVALID_ARG),
     (dict(scale=0.0), B.ERR_INVALID_ARG),

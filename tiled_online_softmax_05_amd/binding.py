@@ -20,7 +20,7 @@ _lib = None
 _lock = threading.Lock()
 
 # attn_dtype
-F32, BF16, BF16_OUT_F32 = 0, 1, 2
+F32, BF16, BF16_OUT_F32, F16, F16_OUT_F32 = 0, 1, 2, 3, 4
 # attn_status
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
 STATUS_NAMES = {OK: "ATTN_OK", ERR_INVALID_ARG: "ATTN_ERR_INVALID_ARG",
@@ -123,6 +123,12 @@ def _dtype_code(t: torch.dtype, out_dtype: Optional[torch.dtype]) -> int:
         if out_dtype == torch.float32:
             return BF16_OUT_F32
         raise ValueError("bf16 inputs produce a bf16 or fp32 output")
+    if t == torch.float16:
+        if out_dtype in (None, torch.float16):
+            return F16
+        if out_dtype == torch.float32:
+            return F16_OUT_F32
+        raise ValueError("fp16 inputs produce an fp16 or fp32 output")
     raise TypeError(f"unsupported input dtype {t}")
 
 
@@ -159,7 +165,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     """O, LSE = attention(q, k, v) on the GPU through ``attn_fwd``.
 
     ``q`` is ``[B, H, Sq, d]``, ``k`` and ``v`` ``[B, H, Skv, d]``, contiguous
-    CUDA(HIP) tensors of one dtype (float32 or bfloat16).  ``scale`` defaults to
+    CUDA(HIP) tensors of one dtype (float32, bfloat16 or float16).  ``scale`` defaults to
     ``1/sqrt(d)``.  ``tiles=(block_m, block_n)`` forces a tile shape.
     ``splits`` (an int, 0 = the library's choice) calls ``attn_fwd_split``
     instead, with a workspace allocated here.  The call is enqueued on torch's
@@ -178,7 +184,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         raise ValueError("q, k, v must be contiguous")
     Skv = k.shape[2]
     code = _dtype_code(q.dtype, out_dtype)
-    odt = torch.float32 if code in (F32, BF16_OUT_F32) else torch.bfloat16
+    odt = {F32: torch.float32, BF16_OUT_F32: torch.float32, F16_OUT_F32: torch.float32,
+           BF16: torch.bfloat16, F16: torch.float16}[code]
     if out is None:
         out = torch.empty((B, H, Sq, d), dtype=odt, device=q.device)
     elif out.shape != (B, H, Sq, d) or out.dtype != odt or not out.is_contiguous():

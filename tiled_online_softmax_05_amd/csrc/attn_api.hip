@@ -61,7 +61,7 @@ constexpr int kMergeBatch = 8;
 
 __global__ void merge_kernel(const float* __restrict__ part_o,
                              const double* __restrict__ part_lse, void* __restrict__ o,
-                             int o_bytes, float* __restrict__ lse, size_t rows, int d,
+                             int o_kind, float* __restrict__ lse, size_t rows, int d,
                              int n_splits) {
     const int d4 = d / 4;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -103,13 +103,16 @@ __global__ void merge_kernel(const float* __restrict__ part_o,
         M = mn;
     }
     const double inv = W > 0.0 ? 1.0 / W : 0.0;
-    if (o_bytes == 4) {
+    if (o_kind == 0) {
         const f32x4 v = {(float)(acc[0] * inv), (float)(acc[1] * inv), (float)(acc[2] * inv),
                          (float)(acc[3] * inv)};
         *reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * d + ch) = v;
-    } else {
+    } else if (o_kind == 1) {
         __bf16* out = static_cast<__bf16*>(o) + row * d + ch;
         for (int i = 0; i < 4; ++i) out[i] = (__bf16)(float)(acc[i] * inv);
+    } else {
+        _Float16* out = static_cast<_Float16*>(o) + row * d + ch;
+        for (int i = 0; i < 4; ++i) out[i] = (_Float16)(float)(acc[i] * inv);
     }
     if (lse != nullptr && ch == 0) lse[row] = W > 0.0 ? (float)(M + log(W)) : -INFINITY;
 }
@@ -120,8 +123,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+bool known_dtype(int dtype) { return dtype >= ATTN_F32 && dtype <= ATTN_F16_OUT_F32; }
 int in_bytes(int dtype) { return dtype == ATTN_F32 ? 4 : 2; }
-int out_bytes(int dtype) { return dtype == ATTN_BF16 ? 2 : 4; }
+int out_bytes(int dtype) { return dtype == ATTN_BF16 || dtype == ATTN_F16 ? 2 : 4; }
+// output element of the merge kernel: 0 fp32, 1 bf16, 2 fp16
+int out_kind(int dtype) { return dtype == ATTN_BF16 ? 1 : (dtype == ATTN_F16 ? 2 : 0); }
 
 // The selector.  Query rows per workgroup shrink until the grid has at
 // least one workgroup per compute unit (256 on MI355X) or the smallest
@@ -142,7 +148,7 @@ int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
         return ATTN_OK;
     }
     if (!(d == 64 || d == 128))
-        return fail(ATTN_ERR_UNSUPPORTED, "bf16 head dim %d not built (64, 128)", d);
+        return fail(ATTN_ERR_UNSUPPORTED, "16-bit head dim %d not built (64, 128)", d);
     // Workgroups of 128 query rows (four waves, two workgroups per CU) when
     // that gives every CU a workgroup, else 64; causal workgroups take a heavy
     // and a light query tile each.  32-key tiles: the pipelined kernel holds
@@ -188,8 +194,7 @@ void split_plan(const Tiles& t, int Sq, int Skv, int BH, int dtype, bool causal,
 }
 
 int validate(const Problem& p) {
-    if (p.dtype != ATTN_F32 && p.dtype != ATTN_BF16 && p.dtype != ATTN_BF16_OUT_F32)
-        return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", p.dtype);
+    if (!known_dtype(p.dtype)) return fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", p.dtype);
     if (p.B < 0 || p.H < 0 || p.Sq < 0 || p.Skv < 0)
         return fail(ATTN_ERR_INVALID_ARG, "negative size (B=%d H=%d Sq=%d Skv=%d)", p.B, p.H,
                     p.Sq, p.Skv);
@@ -304,7 +309,7 @@ hipError_t launch_merge(const Problem& p) {
     const size_t threads = rows * (p.d / 4);
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(256), 0, p.stream, p.part_o,
-                       p.part_lse, p.o, out_bytes(p.dtype), p.lse, rows, p.d, p.n_splits);
+                       p.part_lse, p.o, out_kind(p.dtype), p.lse, rows, p.d, p.n_splits);
     return hipGetLastError();
 }
 
@@ -331,7 +336,7 @@ int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* 
 
 int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal, int* block_m,
                       int* block_n, int* waves, int* lds_bytes) {
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_BF16_OUT_F32)
+    if (!attn::known_dtype(dtype))
         return attn::fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     if (causal != 0 && causal != 1)
         return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);

@@ -1,4 +1,5 @@
-// bf16 attention forward for gfx950 (bf16 MFMA, fp32 accumulation).
+// 16-bit attention forward for gfx950: bf16 or fp16 inputs on the matching
+// MFMA, fp32 accumulation (one template, instantiated for both types).
 //
 // The online softmax of "Tiled attention: preserving results without a full
 // score matrix" (section "Online normalization") over query tiles and key
@@ -7,7 +8,7 @@
 // tile staged in LDS.  The next tile's HBM loads are issued before the
 // current tile is computed, so they overlap with the MFMA work.
 //
-// Contractions use v_mfma_f32_32x32x16_bf16 (A 32x16, B 16x32, D 32x32):
+// Contractions use v_mfma_f32_32x32x16_bf16 / _f16 (A 32x16, B 16x32, D 32x32):
 //   lane = 32 h + c (h in 0..1, c in 0..31);
 //   A: lane holds A[c][8h .. 8h+7];  B: lane holds B[8h .. 8h+7][c];
 //   D: lane holds D[8 (r/4) + 4 h + (r%4)][c] for r = 0..15.
@@ -27,6 +28,7 @@
 // l and the accumulator are rescaled by 2^(m_old - m_new) -- the online
 // normalisation with a relaxed choice of reference point, which gives the
 // same O and LSE up to rounding.
+#include "attn.h"
 #include "attn_internal.h"
 #include "attn_device.h"
 
@@ -137,6 +139,16 @@ __device__ __forceinline__ float other_half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The score and P.V contraction for either 16-bit input type (A 32x16, B
+// 16x32, fp32 D 32x32; the same lane layout for both).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c, int, int, int) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c, int, int, int) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 // Software-pipelined main loop.  Step j holds K_{j+1} and V_j in LDS (two
 // buffers each, chosen by the parity of j) and the raw scores S_j in
 // registers.  Phase A: the matrix cores compute S_{j+1} = K_{j+1} Q^T while
@@ -149,13 +161,15 @@ __device__ __forceinline__ float other_half_sum(float x) {
 // instruction order is fixed by hand (sched_barrier fences): every MFMA
 // operand is read from LDS two MFMAs ahead of its use, and the VALU work is
 // cut into slices placed between consecutive MFMAs.
-template <int D, int BN, int WAVES, bool CAUSAL, bool OUT_F32>
+template <typename T, int D, int BN, int WAVES, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                          const __bf16* __restrict__ V, void* __restrict__ Out,
+void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                          const T* __restrict__ V, void* __restrict__ Out,
                           float* __restrict__ LSE, int n_bh, int Sq, int Skv, float sl2,
                           int n_qt, int kv_chunk, float* __restrict__ part_o,
                           double* __restrict__ part_lse) {
+    typedef T V8 __attribute__((ext_vector_type(8)));   // MFMA operand: 8 elements
+    typedef T V4 __attribute__((ext_vector_type(4)));
     constexpr int BM = 32 * WAVES;
     constexpr int NT = 64 * WAVES;
     constexpr int KS = D / 16;         // k-steps of the score contraction
@@ -177,12 +191,12 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // sV[t % 3], and tiles are fetched two steps ahead of their use.
     // Separate arrays (not one indexed at run time) let the compiler see that
     // the DMA into one buffer never aliases reads of another.
-    __shared__ __attribute__((aligned(16))) __bf16 sK0[BN * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sK1[BN * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sK2[BN * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sV0[BN * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sV1[BN * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sV2[BN * D];
+    __shared__ __attribute__((aligned(16))) T sK0[BN * D];
+    __shared__ __attribute__((aligned(16))) T sK1[BN * D];
+    __shared__ __attribute__((aligned(16))) T sK2[BN * D];
+    __shared__ __attribute__((aligned(16))) T sV0[BN * D];
+    __shared__ __attribute__((aligned(16))) T sV1[BN * D];
+    __shared__ __attribute__((aligned(16))) T sV2[BN * D];
     // vmcnt value that leaves exactly one step's DMA (K and V) in flight
     constexpr int kWaitOlderDma = wait_vmcnt(2 * PER);
     static_assert(3 * PER < 64, "DMA counts must fit the 6-bit vmcnt field");
@@ -209,9 +223,9 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const int c = lane & 31;
     const int off = Skv - Sq;
 
-    const __bf16* Qh = Q + (size_t)bh * Sq * D;
-    const __bf16* Kh = K + (size_t)bh * Skv * D;
-    const __bf16* Vh = V + (size_t)bh * Skv * D;
+    const T* Qh = Q + (size_t)bh * Sq * D;
+    const T* Kh = K + (size_t)bh * Skv * D;
+    const T* Vh = V + (size_t)bh * Skv * D;
 
     // ---- K/V staging: HBM -> LDS by DMA ----
     // Slot S = i * NT + tid (16 bytes) of LDS row S / DCH holds chunk
@@ -220,11 +234,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // rows at or past Skv fall outside its range and read 0; the tile offset
     // moves the base on the scalar unit and each lane's offset within a tile
     // is fixed for the whole kernel.
-    auto tile_words = [&](const __bf16* head, int kv0) {
+    auto tile_words = [&](const T* head, int kv0) {
         const int k0 = min(kv0, Skv);
         return buffer_words(head + (size_t)k0 * D, (uint32_t)(Skv - k0) * ROWB);
     };
-    auto load_k = [&](int kv0, __bf16* dst) {
+    auto load_k = [&](int kv0, T* dst) {
         const i32x4 r = tile_words(Kh, kv0);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -235,7 +249,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             dma16(r, lds_addr(dst + (i * NT + wave * 64) * 8), (uint32_t)key * ROWB + 16 * chunk);
         }
     };
-    auto load_v = [&](int kv0, __bf16* dst) {
+    auto load_v = [&](int kv0, T* dst) {
         const i32x4 r = tile_words(Vh, kv0);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -252,13 +266,13 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     const int qi = q0w + c;
 
     // Q^T operand: lane holds q[qi][16 ks + 8 h .. +7]; rows past Sq read 0
-    bf16x8 qop[KS];
+    V8 qop[KS];
     {
         const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Qh, (uint32_t)Sq * ROWB);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const u32x4 x = buffer_load16(rq, (uint32_t)qi * ROWB + 32 * ks + 16 * h);
-            qop[ks] = __builtin_bit_cast(bf16x8, x);
+            qop[ks] = __builtin_bit_cast(V8, x);
         }
         // Retire the Q loads here, on every path: vmcnt is in-order, and Q
         // loads still in flight at the loop entry would make every tile wait
@@ -286,25 +300,25 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // ---- operand reads ----
     // phase-A MFMA t: key block kb = t % NKB, k-step ks = t / NKB (the two
     // accumulators alternate)
-    auto k_operand = [&](const __bf16* sk, int t) -> bf16x8 {
+    auto k_operand = [&](const T* sk, int t) -> V8 {
         const int kb = t % NKB, ks = t / NKB;
         const int row = kb * 32 + c;
-        return *reinterpret_cast<const bf16x8*>(sk + row * D + 8 * ((2 * ks + h) ^ k_swz(row)));
+        return *reinterpret_cast<const V8*>(sk + row * D + 8 * ((2 * ks + h) ^ k_swz(row)));
     };
     // phase-B MFMA t: k-step s = t / ND (keys 16 s .. 16 s + 15), channel
     // block i = t % ND; two transposing reads, keys 8 h + 4 u .. + 3
     const int g16 = lane & 15;
     const int cblk = lane & 16;
-    auto v_operand = [&](const __bf16* sv, int t) -> bf16x8 {
+    auto v_operand = [&](const T* sv, int t) -> V8 {
         const int s = t / ND, i = t % ND;
-        bf16x4 part[2];
+        V4 part[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int key = 16 * s + 8 * h + 4 * u + (g16 >> 2);
             const int d = 32 * i + cblk + 4 * (g16 & 3);
-            const __bf16* src = sv + key * D + 8 * ((d >> 3) ^ v_swz(key)) + (d & 7);
+            const T* src = sv + key * D + 8 * ((d >> 3) ^ v_swz(key)) + (d & 7);
             part[u] = __builtin_bit_cast(
-                bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4*)(src)));
         }
         return __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -332,14 +346,14 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // PV).  Score and P.V MFMAs alternate, so each has softmax work to hide
     // under it.  The accumulator is moved to the new reference only after
     // the P.V MFMAs, and only when some row of the wave raised it.
-    auto fused = [&](auto QK, auto PV, const __bf16* __restrict__ sk,
-                     const __bf16* __restrict__ sv, const f32x16* st, f32x16* sn,
-                     const bf16x8 (*po)[2], bf16x8 (*pn)[2]) {
+    auto fused = [&](auto QK, auto PV, const T* __restrict__ sk,
+                     const T* __restrict__ sv, const f32x16* st, f32x16* sn,
+                     const V8 (*po)[2], V8 (*pn)[2]) {
         constexpr bool qk = decltype(QK)::value;
         constexpr bool pv = decltype(PV)::value;
         constexpr int NM = (qk ? NA : 0) + (pv ? NB : 0);   // MFMAs of the step
         constexpr int NS = NM > 4 ? NM : 4;                  // schedule slots
-        bf16x8 ka[3], va[3];
+        V8 ka[3], va[3];
         if constexpr (qk) {
             ka[0] = k_operand(sk, 0);
             ka[1] = k_operand(sk, 1);
@@ -360,11 +374,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                 psum += ex[e];
                 if ((e & 7) == 7) {
                     const int b = e - 7;
-                    bf16x8& pk = pn[e / 16][(e / 8) & 1];
+                    V8& pk = pn[e / 16][(e / 8) & 1];
                     pk = __builtin_convertvector(
                         (f32x8){ex[b], ex[b + 1], ex[b + 2], ex[b + 3], ex[b + 4], ex[b + 5],
                                 ex[b + 6], ex[b + 7]},
-                        bf16x8);
+                        V8);
                     pin(pk);
                 }
             }
@@ -380,11 +394,11 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             } else if (is_qk) {
                 if (t + 2 < NA) ka[(t + 2) % 3] = k_operand(sk, t + 2);
                 const int kb = t % NKB, ks = t / NKB;
-                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t % 3], qop[ks], sn[kb], 0, 0, 0);
+                sn[kb] = mfma_32x32x16(ka[t % 3], qop[ks], sn[kb], 0, 0, 0);
             } else {
                 if (t + 2 < NB) va[(t + 2) % 3] = v_operand(sv, t + 2);
                 const int u = t / ND, i = t % ND;
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], po[u / 2][u % 2],
+                acc[i] = mfma_32x32x16(va[t % 3], po[u / 2][u % 2],
                                                                  acc[i], 0, 0, 0);
             }
             if (s == 0) {
@@ -433,15 +447,15 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     using T_ = integral_constant<bool, true>;
     using F_ = integral_constant<bool, false>;
     // P.V of the last tile: acc += P V from sv.
-    auto pv_tile = [&](const __bf16* sv, const bf16x8 (*p)[2]) {
-        bf16x8 va[3];
+    auto pv_tile = [&](const T* sv, const V8 (*p)[2]) {
+        V8 va[3];
         va[0] = v_operand(sv, 0);
         va[1] = v_operand(sv, 1);
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
             if (t + 2 < NB) va[(t + 2) % 3] = v_operand(sv, t + 2);
             const int u = t / ND, i = t % ND;
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t % 3], p[u / 2][u % 2], acc[i],
+            acc[i] = mfma_32x32x16(va[t % 3], p[u / 2][u % 2], acc[i],
                                                              0, 0, 0);
         }
     };
@@ -455,15 +469,15 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     // carries scoped no-alias metadata, which lets the compiler see that the
     // DMA into the free buffers never overlaps the operand reads of the busy
     // ones (the transposing read otherwise waits for all DMA in flight).
-    auto step = [&](auto PV, int j, f32x16* st, bf16x8 (*po)[2],
-                    const __bf16* __restrict__ k_next, __bf16* __restrict__ k_free,
-                    const __bf16* __restrict__ v_prev, __bf16* __restrict__ v_free) {
+    auto step = [&](auto PV, int j, f32x16* st, V8 (*po)[2],
+                    const T* __restrict__ k_next, T* __restrict__ k_free,
+                    const T* __restrict__ v_prev, T* __restrict__ v_free) {
         const int kv0 = kv_begin + j * BN;
         load_k(kv0 + 3 * BN, k_free);           // K_{j+3}: zero rows or unused past the end
         load_v(kv0 + BN, v_free);               // V_{j+1}
         mask(kv0, st);
         f32x16 sn[NKB];
-        bf16x8 pn[NKB][2];
+        V8 pn[NKB][2];
         fused(T_{}, PV, k_next, v_prev, st, sn, po, pn);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -489,7 +503,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
             st[kb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(sK0, ks * NKB + kb),
+                st[kb] = mfma_32x32x16(k_operand(sK0, ks * NKB + kb),
                                                                  qop[ks], st[kb], 0, 0, 0);
         }
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER));   // K_1 has landed
@@ -497,7 +511,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
 
         // ---- steps 0 .. n_tiles - 2 (each has a next tile) ----
         // buffers of step j: K_{j+1}, free slot of K_j, V_{j-1}, free slot of V_{j-2}
-        bf16x8 po[NKB][2];      // probabilities of the previous tile
+        V8 po[NKB][2];      // probabilities of the previous tile
         int j = 0;
         if (n_tiles > 1) {
             step(F_{}, 0, st, po, sK1, sK0, sV2, sV1);     // no P.V yet
@@ -522,10 +536,10 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         const int r = j % 3;
-        const __bf16* v_prev = r == 0 ? sV2 : (r == 1 ? sV0 : sV1);
-        const __bf16* v_last = r == 0 ? sV0 : (r == 1 ? sV1 : sV2);
+        const T* v_prev = r == 0 ? sV2 : (r == 1 ? sV0 : sV1);
+        const T* v_last = r == 0 ? sV0 : (r == 1 ? sV1 : sV2);
         mask(kv_begin + j * BN, st);
-        bf16x8 pn[NKB][2];
+        V8 pn[NKB][2];
         if (j > 0)
             fused(F_{}, T_{}, nullptr, v_prev, st, nullptr, po, pn);
         else
@@ -565,8 +579,8 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
                     if constexpr (OUT_F32) {
                         *reinterpret_cast<f32x4*>(static_cast<float*>(Out) + obase + ch) = o4;
                     } else {
-                        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + obase + ch) =
-                            __builtin_convertvector(o4, bf16x4);
+                        *reinterpret_cast<V4*>(static_cast<T*>(Out) + obase + ch) =
+                            __builtin_convertvector(o4, V4);
                     }
                 }
             if (LSE != nullptr && h == 0)
@@ -582,7 +596,7 @@ void attn_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict
     }
 }
 
-template <int D, int BN, int WAVES, bool OUT_F32>
+template <typename T, int D, int BN, int WAVES, bool OUT_F32>
 hipError_t launch_one(const Problem& p) {
     constexpr int BM = 32 * WAVES;
     const int n_bh = p.B * p.H;
@@ -590,29 +604,29 @@ hipError_t launch_one(const Problem& p) {
     const dim3 grid((unsigned)(n_bh * tile_pair_count(n_qt, p.causal)), (unsigned)p.n_splits);
     const dim3 block(64 * WAVES);
     const float sl2 = p.scale * kLog2ef;
-    const __bf16* q = static_cast<const __bf16*>(p.q);
-    const __bf16* k = static_cast<const __bf16*>(p.k);
-    const __bf16* v = static_cast<const __bf16*>(p.v);
+    const T* q = static_cast<const T*>(p.q);
+    const T* k = static_cast<const T*>(p.k);
+    const T* v = static_cast<const T*>(p.v);
     if (p.causal)
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, WAVES, true, OUT_F32>), grid, block, 0,
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<T, D, BN, WAVES, true, OUT_F32>), grid, block, 0,
                            p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt,
                            p.kv_chunk, p.part_o, p.part_lse);
     else
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, BN, WAVES, false, OUT_F32>), grid, block, 0,
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<T, D, BN, WAVES, false, OUT_F32>), grid, block, 0,
                            p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt,
                            p.kv_chunk, p.part_o, p.part_lse);
     return hipGetLastError();
 }
 
-template <int D, bool OUT_F32>
+template <typename T, int D, bool OUT_F32>
 hipError_t by_tiles(const Problem& p, int bm, int bn) {
     if constexpr (D == 128) {
-        if (bm == 256 && bn == 32) return launch_one<D, 32, 8, OUT_F32>(p);
+        if (bm == 256 && bn == 32) return launch_one<T, D, 32, 8, OUT_F32>(p);
     }
-    if (bm == 128 && bn == 64) return launch_one<D, 64, 4, OUT_F32>(p);
-    if (bm == 128 && bn == 32) return launch_one<D, 32, 4, OUT_F32>(p);
-    if (bm == 64 && bn == 64) return launch_one<D, 64, 2, OUT_F32>(p);
-    if (bm == 64 && bn == 32) return launch_one<D, 32, 2, OUT_F32>(p);
+    if (bm == 128 && bn == 64) return launch_one<T, D, 64, 4, OUT_F32>(p);
+    if (bm == 128 && bn == 32) return launch_one<T, D, 32, 4, OUT_F32>(p);
+    if (bm == 64 && bn == 64) return launch_one<T, D, 64, 2, OUT_F32>(p);
+    if (bm == 64 && bn == 32) return launch_one<T, D, 32, 2, OUT_F32>(p);
     return hipErrorInvalidValue;
 }
 
@@ -628,14 +642,26 @@ int bf16_lds_bytes(int d, int /*block_m*/, int block_n) {
     return 3 * 2 * block_n * d * 2;   // K and V, three buffers each
 }
 
+namespace {
+template <typename T>
+hipError_t by_dim(const Problem& p, const Tiles& t, bool out_f32) {
+    if (p.d == 128)
+        return out_f32 ? by_tiles<T, 128, true>(p, t.block_m, t.block_n)
+                       : by_tiles<T, 128, false>(p, t.block_m, t.block_n);
+    return out_f32 ? by_tiles<T, 64, true>(p, t.block_m, t.block_n)
+                   : by_tiles<T, 64, false>(p, t.block_m, t.block_n);
+}
+}  // namespace
+
 hipError_t launch_bf16(const Problem& p, const Tiles& t) {
     if (!bf16_tiles_supported(p.d, t.block_m, t.block_n)) return hipErrorInvalidValue;
-    const bool out_f32 = p.dtype == 2;
-    if (p.d == 128)
-        return out_f32 ? by_tiles<128, true>(p, t.block_m, t.block_n)
-                       : by_tiles<128, false>(p, t.block_m, t.block_n);
-    return out_f32 ? by_tiles<64, true>(p, t.block_m, t.block_n)
-                   : by_tiles<64, false>(p, t.block_m, t.block_n);
+    switch (p.dtype) {
+        case ATTN_BF16: return by_dim<__bf16>(p, t, false);
+        case ATTN_BF16_OUT_F32: return by_dim<__bf16>(p, t, true);
+        case ATTN_F16: return by_dim<_Float16>(p, t, false);
+        case ATTN_F16_OUT_F32: return by_dim<_Float16>(p, t, true);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace attn
