@@ -22,9 +22,10 @@ widen to float64 exactly.
 Readings taken where the pages are silent (each is also listed in the design
 notes):
 
-* Causal visibility for Sq != Skv is bottom-right aligned: query row ``i``
-  sees key ``j`` iff ``j <= i + (Skv - Sq)``.  The pages only use Sq == Skv,
-  where this is their ``j <= i`` rule.
+* Causal visibility for Sq != Skv is bottom-right aligned by default: query
+  row ``i`` sees key ``j`` iff ``j <= i + (Skv - Sq)``.  The pages only use
+  Sq == Skv, where this is their ``j <= i`` rule.  ``align="start"`` takes the
+  rule literally instead (``j <= i``, top-left aligned) for the other reading.
 * A row that sees no key gets O = 0 and LSE = -inf (the online-normalization
   section says such rows need separate handling; it does not say how).
 * LSE is the natural log of the sum of exponentials of the *scaled* scores.
@@ -49,20 +50,24 @@ def _as_f64(x) -> np.ndarray:
     return a.astype(np.float64, copy=False)
 
 
-def last_visible_key(i: int, Sq: int, Skv: int, causal: bool) -> int:
+def last_visible_key(i: int, Sq: int, Skv: int, causal: bool, align: str = "end") -> int:
     """Index one past the last key row ``i`` may attend to.
 
     Non-causal rows see every key.  Causal rows see keys ``j <= i + Skv - Sq``
     (the ``j <= i`` rule of the direct lab function on "Verify tiled
     attention", section "Compare the attention outputs", aligned to the end of
-    the key sequence when Sq != Skv).  The result is clamped to [0, Skv]."""
+    the key sequence when Sq != Skv), or ``j <= i`` with ``align="start"``.
+    The result is clamped to [0, Skv]."""
     if not causal:
         return Skv
-    return max(0, min(Skv, i + (Skv - Sq) + 1))
+    if align not in ("end", "start"):
+        raise ValueError("align is 'end' or 'start'")
+    offset = Skv - Sq if align == "end" else 0
+    return max(0, min(Skv, i + offset + 1))
 
 
 def _rows_direct(q_rows: np.ndarray, row_ids: Sequence[int], k: np.ndarray, v: np.ndarray,
-                 Sq: int, scale: float, causal: bool, subtract_max: bool
+                 Sq: int, scale: float, causal: bool, subtract_max: bool, align: str = "end"
                  ) -> Tuple[np.ndarray, np.ndarray, int]:
     """Direct attention for a set of query rows of one head, materialising
     each row's full score vector and probability vector (the three steps of
@@ -78,7 +83,7 @@ def _rows_direct(q_rows: np.ndarray, row_ids: Sequence[int], k: np.ndarray, v: n
     # 1. scores s_ij = scale * q_i . k_j for every key (library matmul as one step)
     scores = (q_rows @ k.T) * scale
     for r, i in enumerate(row_ids):
-        n = last_visible_key(int(i), Sq, Skv, causal)
+        n = last_visible_key(int(i), Sq, Skv, causal, align)
         if n == 0:
             continue                      # no visible key: O = 0, LSE = -inf
         s = scores[r, :n]
@@ -99,7 +104,7 @@ def _rows_direct(q_rows: np.ndarray, row_ids: Sequence[int], k: np.ndarray, v: n
 
 def direct_attention(q, k, v, scale: float | None = None, causal: bool = False,
                      subtract_max: bool = True, row_chunk: int = 256,
-                     return_meta: bool = False):
+                     return_meta: bool = False, align: str = "end"):
     """Exact scaled-dot-product attention forward, the definition that the
     tiled method reaches up to rounding ("Keep the softmax state between
     tiles" on "Verify tiled attention"; "Correctness first" on
@@ -112,7 +117,8 @@ def direct_attention(q, k, v, scale: float | None = None, causal: bool = False,
     and ``LSE_i = m_i + ln l_i``.  Rows without a visible key give O = 0 and
     LSE = -inf.  ``subtract_max=False`` is the unshifted softmax of the
     overflow check in "Read the executable checks"; it raises
-    ``OverflowError`` when an exponential overflows.
+    ``OverflowError`` when an exponential overflows.  ``align`` chooses the
+    causal alignment (see ``last_visible_key``).
 
     Rows are processed in chunks of ``row_chunk`` (full rows each, no running
     state carried between chunks).  Returns ``(O, LSE)`` as float64, plus a
@@ -137,7 +143,7 @@ def direct_attention(q, k, v, scale: float | None = None, causal: bool = False,
         for r0 in range(0, Sq, row_chunk):
             rows = list(range(r0, min(Sq, r0 + row_chunk)))
             o_c, l_c, n_c = _rows_direct(qf[h, rows], rows, kf[h], vf[h], Sq, scale,
-                                         causal, subtract_max)
+                                         causal, subtract_max, align)
             out[h, r0:r0 + len(rows)] = o_c
             lse[h, r0:r0 + len(rows)] = l_c
             materialised += n_c
@@ -149,14 +155,15 @@ def direct_attention(q, k, v, scale: float | None = None, causal: bool = False,
 
 
 def direct_attention_rows(q_head, row_ids: Sequence[int], k_head, v_head, Sq: int,
-                          scale: float, causal: bool) -> Tuple[np.ndarray, np.ndarray]:
+                          scale: float, causal: bool, align: str = "end"
+                          ) -> Tuple[np.ndarray, np.ndarray]:
     """Direct attention for selected query rows ``row_ids`` of one head.
     ``q_head`` holds exactly those rows (``[len(row_ids), d]``); ``k_head`` and
     ``v_head`` are the head's full ``[Skv, d]`` keys and values, and ``Sq`` is
     the head's full query length (needed for the causal offset).  Used to check
     sampled outputs at sizes where the whole output would take too long."""
     o, l, _ = _rows_direct(_as_f64(q_head), list(row_ids), _as_f64(k_head), _as_f64(v_head),
-                           Sq, scale, causal, True)
+                           Sq, scale, causal, True, align)
     return o, l
 
 
