@@ -19,10 +19,11 @@
  * end.  The score matrix never leaves the chip.
  *
  * Visibility: key j is visible to query row i iff j < Skv and, for causal
- * attention, j <= i + (Skv - Sq) (the "j <= i" causal rule of the lab page,
- * aligned to the end of the key sequence when Sq != Skv).  A row with no
- * visible key (Skv == 0, or causal with i < Sq - Skv) gets O = 0 and
- * LSE = -inf; no NaN is produced.
+ * attention (causal = 1), j <= i + (Skv - Sq): the "j <= i" causal rule of
+ * the lab page, aligned to the end of the key sequence when Sq != Skv.
+ * causal = 2 aligns the rule to the start instead (j <= i).  The two agree
+ * when Sq == Skv.  A row with no visible key (Skv == 0, or end-aligned causal
+ * with i < Sq - Skv) gets O = 0 and LSE = -inf; no NaN is produced.
  *
  * Layout (all tensors dense, row-major, the head dimension fastest):
  *     q, o : [B, H, Sq,  d]
@@ -66,7 +67,7 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1,  /* null pointer for a non-empty tensor, negative
                                   size, non-finite or non-positive scale,
-                                  unknown dtype, causal not 0/1, size overflow,
+                                  unknown dtype, causal not 0/1/2, size overflow,
                                   o aliasing an input                         */
     ATTN_ERR_UNSUPPORTED = 2,  /* head dim or forced tile shape not built      */
     ATTN_ERR_MISALIGNED = 3,   /* a pointer not 16-byte aligned                */
@@ -84,7 +85,7 @@ typedef enum {
  *   d        : head dimension: 16, 32, 64 or 128 (fp32); 64 or 128 (bf16,
  *              fp16).
  *   scale    : score scale, finite and > 0 (usually 1/sqrt(d)).
- *   causal   : 0 or 1 (end-aligned mask above).
+ *   causal   : 0 (none), 1 (end-aligned mask above) or 2 (start-aligned).
  *   dtype    : an attn_dtype.
  *   stream   : hipStream_t or NULL.
  * Returns an attn_status; on failure attn_last_error() describes it and

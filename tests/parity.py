@@ -83,8 +83,11 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, o_tol: float, lse_tol: float, what: 
     return worst, lworst
 
 
-def oracle_full(q, k, v, causal: bool, scale: Optional[float] = None):
-    return oracle.direct_attention(to_f64(q), to_f64(k), to_f64(v), scale=scale, causal=causal)
+def oracle_full(q, k, v, causal, scale: Optional[float] = None):
+    """``causal``: False, True (end-aligned) or 2 (start-aligned), as the ABI."""
+    align = "start" if causal == 2 else "end"
+    return oracle.direct_attention(to_f64(q), to_f64(k), to_f64(v), scale=scale,
+                                   causal=bool(causal), align=align)
 
 
 def check_full(q, k, v, causal: bool, scale=None, out_dtype=None, tiles=None, what="",

@@ -101,7 +101,8 @@ def _call(lib, q=A0, k=A1, v=A2, o=A3, lse=A4, Bn=1, H=2, Sq=64, Skv=64, d=64, s
     (dict(scale=float("inf")), B.ERR_INVALID_ARG),
     (dict(scale=0.0), B.ERR_INVALID_ARG),
     (dict(scale=-0.5), B.ERR_INVALID_ARG),
-    (dict(causal=2), B.ERR_INVALID_ARG),
+    (dict(causal=3), B.ERR_INVALID_ARG),
+    (dict(causal=-1), B.ERR_INVALID_ARG),
     (dict(q=A0 + 4), B.ERR_MISALIGNED),
     (dict(o=A3 + 8), B.ERR_MISALIGNED),
     (dict(lse=A4 + 2), B.ERR_MISALIGNED),
@@ -180,7 +181,8 @@ def _split(lib, n_splits=2, ws=0x600000, ws_bytes=1 << 20, **kw):
     (dict(ws=0x600000 + 16), B.ERR_MISALIGNED),
     (dict(ws=A3), B.ERR_INVALID_ARG),                         # overlaps o
     (dict(ws=A0), B.ERR_INVALID_ARG),                         # overlaps q
-    (dict(causal=2), B.ERR_INVALID_ARG),
+    (dict(causal=3), B.ERR_INVALID_ARG),
+    (dict(causal=-1), B.ERR_INVALID_ARG),
     (dict(d=48), B.ERR_UNSUPPORTED),
     (dict(n_splits=0, ws=None, Sq=8, Skv=1000, d=32), B.ERR_INVALID_ARG),  # auto split, no workspace
 ])

@@ -21,6 +21,8 @@ _lock = threading.Lock()
 
 # attn_dtype
 F32, BF16, BF16_OUT_F32, F16, F16_OUT_F32 = 0, 1, 2, 3, 4
+# causal argument: no mask, mask aligned to the end of the keys, to their start
+NON_CAUSAL, CAUSAL_END, CAUSAL_START = 0, 1, 2
 # attn_status
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
 STATUS_NAMES = {OK: "ATTN_OK", ERR_INVALID_ARG: "ATTN_ERR_INVALID_ARG",
@@ -167,6 +169,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     ``q`` is ``[B, H, Sq, d]``, ``k`` and ``v`` ``[B, H, Skv, d]``, contiguous
     CUDA(HIP) tensors of one dtype (float32, bfloat16 or float16).  ``scale`` defaults to
     ``1/sqrt(d)``.  ``tiles=(block_m, block_n)`` forces a tile shape.
+    ``causal`` is False/True (end-aligned) or ``CAUSAL_START``.
     ``splits`` (an int, 0 = the library's choice) calls ``attn_fwd_split``
     instead, with a workspace allocated here.  The call is enqueued on torch's
     current stream of q's device."""

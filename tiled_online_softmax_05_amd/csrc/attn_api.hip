@@ -325,12 +325,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int Sq, int Skv, int d, float scale, int causal, int dtype,
                    void* stream, int block_m, int block_n) {
-    if (causal != 0 && causal != 1)
-        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+    if (causal < 0 || causal > 2)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0, 1 or 2 (got %d)", causal);
     if (block_m < 0 || block_n < 0 || ((block_m == 0) != (block_n == 0)))
         return attn::fail(ATTN_ERR_INVALID_ARG, "block_m, block_n must both be 0 or positive");
-    attn::Problem p{q, k, v, o, lse, B, H, Sq, Skv, d, scale, causal == 1, dtype,
+    attn::Problem p{q, k, v, o, lse, B, H, Sq, Skv, d, scale, causal != 0, dtype,
                     static_cast<hipStream_t>(stream)};
+    p.causal_off = causal == 2 ? 0 : Skv - Sq;
     return attn::run(p, block_m, block_n);
 }
 
@@ -338,12 +339,12 @@ int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal, int
                       int* block_n, int* waves, int* lds_bytes) {
     if (!attn::known_dtype(dtype))
         return attn::fail(ATTN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-    if (causal != 0 && causal != 1)
-        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+    if (causal < 0 || causal > 2)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0, 1 or 2 (got %d)", causal);
     if (d <= 0 || Sq < 0 || Skv < 0 || BH < 0)
         return attn::fail(ATTN_ERR_INVALID_ARG, "negative or zero size");
     attn::Tiles t{};
-    const int st = attn::select(d, Sq, Skv, BH, dtype, causal == 1, &t);
+    const int st = attn::select(d, Sq, Skv, BH, dtype, causal != 0, &t);
     if (st != ATTN_OK) return st;
     if (block_m) *block_m = t.block_m;
     if (block_n) *block_n = t.block_n;
@@ -355,13 +356,14 @@ int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal, int
 int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int Sq, int Skv, int d, float scale, int causal, int dtype,
                    void* stream, int n_splits, void* workspace, long long workspace_bytes) {
-    if (causal != 0 && causal != 1)
-        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+    if (causal < 0 || causal > 2)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0, 1 or 2 (got %d)", causal);
     if (n_splits < 0 || n_splits > 4096)
         return attn::fail(ATTN_ERR_INVALID_ARG, "n_splits must be in [0, 4096] (got %d)",
                           n_splits);
-    attn::Problem p{q, k, v, o, lse, B, H, Sq, Skv, d, scale, causal == 1, dtype,
+    attn::Problem p{q, k, v, o, lse, B, H, Sq, Skv, d, scale, causal != 0, dtype,
                     static_cast<hipStream_t>(stream)};
+    p.causal_off = causal == 2 ? 0 : Skv - Sq;
     return attn::run(p, 0, 0, n_splits, workspace, workspace_bytes);
 }
 
@@ -372,7 +374,7 @@ int attn_select_splits(int d, int Sq, int Skv, int BH, int dtype, int causal, in
     if (st != ATTN_OK) return st;
     attn::Tiles t{bm, bn, waves, lds};
     int n = 1, chunk = Skv;
-    if (Skv > 0) attn::split_plan(t, Sq, Skv, BH, dtype, causal == 1, 0, &n, &chunk);
+    if (Skv > 0) attn::split_plan(t, Sq, Skv, BH, dtype, causal != 0, 0, &n, &chunk);
     if (n_splits) *n_splits = n;
     if (kv_chunk) *kv_chunk = chunk;
     return attn::ok();

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                           const T* __restrict__ V, void* __restrict__ Out,
                           float* __restrict__ LSE, int n_bh, int Sq, int Skv, float sl2,
-                          int n_qt, int kv_chunk, float* __restrict__ part_o,
+                          int n_qt, int off, int kv_chunk, float* __restrict__ part_o,
                           double* __restrict__ part_lse) {
     typedef T V8 __attribute__((ext_vector_type(8)));   // MFMA operand: 8 elements
     typedef T V4 __attribute__((ext_vector_type(4)));
@@ -221,7 +221,6 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int c = lane & 31;
-    const int off = Skv - Sq;
 
     const T* Qh = Q + (size_t)bh * Sq * D;
     const T* Kh = K + (size_t)bh * Skv * D;
@@ -292,7 +291,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // key chunk blockIdx.y of the (possibly split) key range
     const int q_last = min(Sq, (qt + 1) * BM) - 1;
     const int kv_begin = (int)blockIdx.y * kv_chunk;
-    const int kv_end = min(kv_limit(q_last, Sq, Skv, CAUSAL), kv_begin + min(kv_chunk, Skv));
+    const int kv_end = min(kv_limit(q_last, off, Skv, CAUSAL), kv_begin + min(kv_chunk, Skv));
     const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BN - 1) / BN : 0;
     // last key this lane's query may see (for the masked tiles)
     const int lim = CAUSAL ? min(Skv - 1, qi + off) : Skv - 1;
@@ -610,11 +609,11 @@ hipError_t launch_one(const Problem& p) {
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<T, D, BN, WAVES, true, OUT_F32>), grid, block, 0,
                            p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt,
-                           p.kv_chunk, p.part_o, p.part_lse);
+                           p.causal_off, p.kv_chunk, p.part_o, p.part_lse);
     else
         hipLaunchKernelGGL((attn_fwd_bf16_kernel<T, D, BN, WAVES, false, OUT_F32>), grid, block, 0,
                            p.stream, q, k, v, p.o, p.lse, n_bh, p.Sq, p.Skv, sl2, n_qt,
-                           p.kv_chunk, p.part_o, p.part_lse);
+                           p.causal_off, p.kv_chunk, p.part_o, p.part_lse);
     return hipGetLastError();
 }
 

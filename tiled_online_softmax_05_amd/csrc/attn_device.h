@@ -56,10 +56,11 @@ __device__ __forceinline__ void tile_pair_coords(int n_bh, int n_qt, bool causal
 }
 
 // Key range [0, kv_end) a workgroup of query rows [q_first, q_last] visits:
-// causal rows see keys j <= i + (Skv - Sq).
-__device__ __forceinline__ int kv_limit(int q_last, int Sq, int Skv, bool causal) {
+// causal rows see keys j <= i + off (off = Skv - Sq when the mask is aligned
+// to the end of the key sequence, 0 when aligned to its start).
+__device__ __forceinline__ int kv_limit(int q_last, int off, int Skv, bool causal) {
     if (!causal) return Skv;
-    int e = q_last + (Skv - Sq) + 1;
+    int e = q_last + off + 1;
     return e < 0 ? 0 : (e > Skv ? Skv : e);
 }
 

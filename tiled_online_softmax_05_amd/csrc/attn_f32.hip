@@ -38,7 +38,7 @@ __global__ __launch_bounds__(64 * WAVES)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, float* __restrict__ O,
                          float* __restrict__ LSE, int n_bh, int Sq, int Skv, double scale,
-                         int n_qt, int kv_chunk, float* __restrict__ part_o,
+                         int n_qt, int off, int kv_chunk, float* __restrict__ part_o,
                          double* __restrict__ part_lse) {
     constexpr int BM = 16 * WAVES;
     constexpr int NT = 64 * WAVES;
@@ -57,7 +57,6 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     const int wave = tid >> 6;
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int off = Skv - Sq;
     const int qi = qt * BM + wave * 16 + c;
 
     const float* Qh = Q + (size_t)bh * Sq * D;
@@ -90,7 +89,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     // key chunk blockIdx.y of the (possibly split) key range
     const int q_last = min(Sq, (qt + 1) * BM) - 1;
     const int kv_begin = (int)blockIdx.y * kv_chunk;
-    const int kv_end = min(kv_limit(q_last, Sq, Skv, CAUSAL), kv_begin + min(kv_chunk, Skv));
+    const int kv_end = min(kv_limit(q_last, off, Skv, CAUSAL), kv_begin + min(kv_chunk, Skv));
 
     for (int kv0 = kv_begin; kv0 < kv_end; kv0 += BN) {
         __syncthreads();
@@ -209,11 +208,11 @@ hipError_t launch_one(const Problem& p) {
     float* o = static_cast<float*>(p.o);
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, true>), grid, block, 0, p.stream,
-                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.kv_chunk,
+                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.causal_off, p.kv_chunk,
                            p.part_o, p.part_lse);
     else
         hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, false>), grid, block, 0, p.stream,
-                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.kv_chunk,
+                           q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.causal_off, p.kv_chunk,
                            p.part_o, p.part_lse);
     return hipGetLastError();
 }

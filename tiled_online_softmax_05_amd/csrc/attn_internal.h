@@ -24,6 +24,9 @@ struct Problem {
     // kernels write each chunk's partial state -- O_c = a_c / l_c (fp32) and
     // LSE_c (fp64) -- to [n_splits, B*H, Sq, d] and [n_splits, B*H, Sq]
     // instead of o and lse, and launch_merge() combines them.
+    // Causal diagonal: query row i sees keys j <= i + causal_off (Skv - Sq for
+    // end-aligned masking, 0 for start-aligned).
+    int causal_off = 0;
     int n_splits = 1;
     int kv_chunk = 0x7FFFFFFF;
     float* part_o = nullptr;
