@@ -365,6 +365,11 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         }
         float mx = -INFINITY, m_ref = 0.f, alpha = 1.f, psum = 0.f;
         bool rescale = false;
+        // While it interleaves MFMAs and softmax, the wave outranks a wave of
+        // the other workgroup on the same SIMD that is issuing DMA, waiting at
+        // its barrier or finishing a step (measured: 2 % faster than equal
+        // priorities; per-MFMA raises were slower).
+        __builtin_amdgcn_s_setprio(2);
         float ex[NV];
         // row sum of values [p0, p1), packed to bf16 in groups of 8
         auto sum_pack = [&](int p0, int p1) {
@@ -432,6 +437,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         sum_pack((NS - 3) * NV / (NS - 2), NV);     // the last slot's values
         l = l * alpha + psum;
         // acc holds sum_{t <= j-1} relative to the old reference; move it to
