@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -41,11 +42,25 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_h32_s4096_d128.js
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_device.h", "attn_api.hip"]
 
 
-def kernel_source_hash() -> str:
+def code_text(src: str) -> str:
+    """The source without comments and blank lines (so that comment edits do
+    not invalidate measurements taken on the same code)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in src.splitlines()]
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the code of the kernel sources (see ``code_text``)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "tiled_online_softmax_05_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        path = os.path.join(ROOT, "tiled_online_softmax_05_amd", "csrc", name)
+        if read is None:
+            with open(path) as f:
+                text = f.read()
+        else:
+            text = read(path)
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,8 +5,8 @@
 // score matrix" (section "Online normalization") over query tiles and key
 // tiles as in the tiled lab function of "Verify tiled attention".  Each
 // 64-wide wave owns 32 query rows; the waves of a workgroup share one K/V
-// tile staged in LDS.  The next tile's HBM loads are issued before the
-// current tile is computed, so they overlap with the MFMA work.
+// tile staged in LDS.  K/V tiles travel HBM -> LDS by DMA two steps ahead
+// of their use, so the loads overlap with the MFMA work.
 //
 // Contractions use v_mfma_f32_32x32x16_bf16 / _f16 (A 32x16, B 16x32, D 32x32):
 //   lane = 32 h + c (h in 0..1, c in 0..31);
@@ -149,15 +149,15 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c, int,
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Software-pipelined main loop.  Step j holds K_{j+1} and V_j in LDS (two
-// buffers each, chosen by the parity of j) and the raw scores S_j in
-// registers.  Phase A: the matrix cores compute S_{j+1} = K_{j+1} Q^T while
-// the VALU runs the online-softmax update of S_j (row max, rescale factor,
-// exponentials, bf16 packing).  Phase B: O^T += V_j^T P_j on the matrix cores
-// while the VALU rescales the accumulator block by block and sums the
-// probabilities.  K_{j+2} and V_{j+1} travel HBM -> LDS by DMA during the step
-// into the buffers freed by step j - 1; one workgroup barrier per step
-// separates a buffer's last read from its next write.  Within a phase the
+// Software-pipelined main loop (skewed).  Step j holds the raw scores S_j in
+// registers and K_{j+1}, V_{j-1} in LDS.  The matrix cores compute
+// S_{j+1} = K_{j+1} Q^T and add P_{j-1} V_{j-1} to the accumulator, the two
+// kinds of MFMA alternating, while the VALU runs the online-softmax update
+// of S_j between them (row max, reference and rescale factor, exponentials,
+// row sums, packing into P_j).  K and V live in three LDS buffers each (K_t
+// in sK[t % 3], V_t in sV[t % 3]); step j starts the DMA of K_{j+3} and
+// V_{j+1} into the buffers its predecessor finished reading and ends with one
+// workgroup barrier after waiting for the DMA issued one step earlier.  The
 // instruction order is fixed by hand (sched_barrier fences): every MFMA
 // operand is read from LDS two MFMAs ahead of its use, and the VALU work is
 // cut into slices placed between consecutive MFMAs.
@@ -179,8 +179,8 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     constexpr int ROWB = D * 2;        // bytes per K/V row
     constexpr int CHUNKS = BN * DCH;   // 16-byte chunks per K or V tile
     constexpr int PER = CHUNKS / NT;   // chunks each thread moves per tile
-    constexpr int NA = NKB * KS;       // MFMAs of phase A (scores)
-    constexpr int NB = 2 * NKB * ND;   // MFMAs of phase B (P.V)
+    constexpr int NA = NKB * KS;       // score MFMAs per step
+    constexpr int NB = 2 * NKB * ND;   // P.V MFMAs per step
     constexpr int NV = 16 * NKB;       // scores per lane per tile
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert(CHUNKS % NT == 0, "every lane moves the same number of chunks");
@@ -297,15 +297,15 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     const int lim = CAUSAL ? min(Skv - 1, qi + off) : Skv - 1;
 
     // ---- operand reads ----
-    // phase-A MFMA t: key block kb = t % NKB, k-step ks = t / NKB (the two
-    // accumulators alternate)
+    // K operand of score MFMA t: key block kb = t % NKB, k-step ks = t / NKB
+    // (the accumulators of the key blocks alternate)
     auto k_operand = [&](const T* sk, int t) -> V8 {
         const int kb = t % NKB, ks = t / NKB;
         const int row = kb * 32 + c;
         return *reinterpret_cast<const V8*>(sk + row * D + 8 * ((2 * ks + h) ^ k_swz(row)));
     };
-    // phase-B MFMA t: k-step s = t / ND (keys 16 s .. 16 s + 15), channel
-    // block i = t % ND; two transposing reads, keys 8 h + 4 u .. + 3
+    // V operand of P.V MFMA t: k-step s = t / ND (keys 16 s .. 16 s + 15),
+    // channel block i = t % ND; two transposing reads, keys 8 h + 4 u .. + 3
     const int g16 = lane & 15;
     const int cblk = lane & 16;
     auto v_operand = [&](const T* sv, int t) -> V8 {
