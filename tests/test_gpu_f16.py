@@ -58,3 +58,11 @@ def test_f16_split_and_edges():
     q, k, v = random_tensors(2, 2, 10, 0, 64, "f16", "normal", seed=46)
     o, lse = gpu_run(q, k, v, False)
     assert torch.all(o == 0) and torch.all(lse == -math.inf)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_batched_heads_16bit(dt):
+    # B > 1: heads of different batch entries must not mix
+    q, k, v = random_tensors(3, 5, 130, 150, 128, dt, "uniform0.8", seed=81)
+    for causal in (False, True):
+        check_full(q, k, v, causal, what=f"{dt} B=3 H=5 130x150 causal={causal}")

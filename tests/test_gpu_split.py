@@ -91,3 +91,27 @@ def test_split_workspace_is_scratch():
     qh, kh, vh = make_tensors(w)
     o_ref, lse_ref = oracle_full(qh, kh, vh, False)
     compare(o, lse, o_ref, lse_ref, O_TOL["f32"], LSE_TOL["f32"], "split over a NaN workspace")
+
+
+def test_split_without_lse_and_with_scales():
+    dev = torch.device("cuda", 0)
+    q, k, v = random_tensors(2, 3, 5, 2000, 64, "bf16", "normal", seed=71)
+    o, lse = binding.fwd(q.to(dev), k.to(dev), v.to(dev), causal=False, with_lse=False,
+                         splits=0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert lse is None
+    o_ref, _ = oracle_full(q, k, v, False)
+    compare(o, None, o_ref, None, O_TOL["bf16"], 0, "split, no LSE")
+    for scale in (0.01, 0.5):
+        check_full(q, k, v, True, scale=scale, splits=0, out_dtype=torch.float32,
+                   what=f"split scale {scale}")
+    q, k, v = random_tensors(1, 2, 8, 1000, 32, "f32", "stress", seed=72)
+    check_full(q, k, v, False, scale=0.3, splits=5, what="f32 split scale 0.3")
+
+
+def test_split_fp32_long_decode():
+    # one query row against 8000 keys, head dim 128, fp32
+    q, k, v = random_tensors(1, 4, 1, 8000, 128, "f32", "normal", seed=73)
+    for causal in (False, True):
+        check_full(q, k, v, causal, splits=0, what=f"f32 decode 1x8000 causal={causal}")
+        check_full(q, k, v, causal, what=f"f32 decode 1x8000 unsplit causal={causal}")
