@@ -165,7 +165,9 @@ def test_select_splits(lib, args, split):
 
 
 def _split(lib, n_splits=2, ws=0x600000, ws_bytes=1 << 20, **kw):
-    base = dict(q=A0, k=A1, v=A2, o=A3, lse=A4, Bn=1, H=2, Sq=64, Skv=64, d=64, scale=0.125,
+    # 1000 keys in 64-key tiles: two requested chunks do run, so each case
+    # below fails validation before any HIP call
+    base = dict(q=A0, k=A1, v=A2, o=A3, lse=A4, Bn=1, H=2, Sq=8, Skv=1000, d=32, scale=0.125,
                 causal=0, dtype=B.F32)
     base.update(kw)
     return lib.attn_fwd_split(base["q"], base["k"], base["v"], base["o"], base["lse"], base["Bn"],
@@ -184,7 +186,8 @@ def _split(lib, n_splits=2, ws=0x600000, ws_bytes=1 << 20, **kw):
     (dict(causal=3), B.ERR_INVALID_ARG),
     (dict(causal=-1), B.ERR_INVALID_ARG),
     (dict(d=48), B.ERR_UNSUPPORTED),
-    (dict(n_splits=0, ws=None, Sq=8, Skv=1000, d=32), B.ERR_INVALID_ARG),  # auto split, no workspace
+    (dict(n_splits=0, ws=None), B.ERR_INVALID_ARG),           # auto split, no workspace
+    (dict(ws_bytes=1 << 10, n_splits=16), B.ERR_INVALID_ARG), # too small for the chunks that run
 ])
 def test_split_invalid_arguments_rejected_on_host(lib, kw, status):
     assert _split(lib, **kw) == status

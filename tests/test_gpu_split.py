@@ -115,3 +115,19 @@ def test_split_fp32_long_decode():
     for causal in (False, True):
         check_full(q, k, v, causal, splits=0, what=f"f32 decode 1x8000 causal={causal}")
         check_full(q, k, v, causal, what=f"f32 decode 1x8000 unsplit causal={causal}")
+
+
+def test_split_workspace_for_the_chunks_that_run():
+    # 64 chunks requested on 2 key tiles: 2 run, and a workspace sized for 2
+    # is enough (the header's contract)
+    q, k, v = [t.cuda() for t in random_tensors(1, 2, 8, 100, 64, "f32", "normal", seed=74)]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], device="cuda")
+    nbytes = binding.split_workspace_bytes(1, 2, 8, 64, 2)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    binding.fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          1, 2, 8, 100, 64, 0.125, False, binding.F32,
+                          torch.cuda.current_stream().cuda_stream, 64, ws.data_ptr(), nbytes)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q.cpu(), k.cpu(), v.cpu(), False, 0.125)
+    compare(o, lse, o_ref, lse_ref, O_TOL["f32"], LSE_TOL["f32"], "64 chunks requested, 2 run")

@@ -129,11 +129,13 @@ int out_bytes(int dtype) { return dtype == ATTN_BF16 || dtype == ATTN_F16 ? 2 : 
 // output element of the merge kernel: 0 fp32, 1 bf16, 2 fp16
 int out_kind(int dtype) { return dtype == ATTN_BF16 ? 1 : (dtype == ATTN_F16 ? 2 : 0); }
 
+// Compute units of an MI355X: the selectors aim to give each one work.
+constexpr long kCUs = 256;
+
 // The selector.  Query rows per workgroup shrink until the grid has at
-// least one workgroup per compute unit (256 on MI355X) or the smallest
-// shape is reached; key rows per tile follow the key length.
+// least one workgroup per compute unit or the smallest shape is reached;
+// key rows per tile follow the key length.
 int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
-    constexpr long kCUs = 256;
     auto wgs = [&](int bm) { return (long)BH * ((Sq + bm - 1) / bm); };
     if (dtype == ATTN_F32) {
         if (!(d == 16 || d == 32 || d == 64 || d == 128))
@@ -180,7 +182,6 @@ int64_t split_workspace(int64_t rows, int d, int n) { return part_o_bytes(rows, 
 // rounded to whole tiles.  Returns the chunk count and length.
 void split_plan(const Tiles& t, int Sq, int Skv, int BH, int dtype, bool causal, int want,
                 int* n_splits, int* kv_chunk) {
-    constexpr long kCUs = 256;
     const long n_qt = (Sq + t.block_m - 1) / t.block_m;
     const long items = (long)BH * (dtype == ATTN_F32 ? n_qt : (causal ? (n_qt + 1) / 2 : n_qt));
     long n = want;
@@ -242,10 +243,7 @@ int run(const Problem& p_in, int block_m, int block_n, int want_splits = -1,
     if (st != ATTN_OK) return st;
     const int bh = p.B * p.H;
     if (want_splits >= 0) {
-        const int64_t need = split_workspace((int64_t)bh * p.Sq, p.d, std::max(want_splits, 1));
-        if (want_splits > 0 && (workspace == nullptr || workspace_bytes < need))
-            return fail(ATTN_ERR_INVALID_ARG, "workspace of %lld bytes too small (need %lld)",
-                        (long long)workspace_bytes, (long long)need);
+        // the size is checked once the chunk count is known (below)
         if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
             return fail(ATTN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
         const size_t ib = (size_t)in_bytes(p.dtype);
