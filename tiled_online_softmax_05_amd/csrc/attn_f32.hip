@@ -91,21 +91,60 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     const int kv_begin = (int)blockIdx.y * kv_chunk;
     const int kv_end = min(kv_limit(q_last, off, Skv, CAUSAL), kv_begin + min(kv_chunk, Skv));
 
+    // K/V tile staging.  Element e (one 16-byte vector) of a tile is row
+    // e / (D/4), vector e % (D/4); rows at or past Skv read as zeros.  When a
+    // thread's share of a tile fits in a few registers (PF vectors per
+    // operand), the next tile is fetched into registers right after the
+    // current one reaches LDS, so its global-memory latency overlaps the
+    // current tile's arithmetic; otherwise each tile is loaded and stored in
+    // one pass.
+    constexpr int NE = BN * (D / 4);
+    constexpr int PF = NE % NT == 0 ? NE / NT : 0;
+    constexpr bool kPrefetch = PF > 0 && PF <= 8;
+    f32x4 kpf[kPrefetch ? PF : 1], vpf[kPrefetch ? PF : 1];
+    auto fetch_vec = [&](int kv0, int e, f32x4& kx, f32x4& vx) {
+        const int row = e / (D / 4);
+        const int c4 = e - row * (D / 4);
+        const int key = kv0 + row;
+        kx = f32x4{0.f, 0.f, 0.f, 0.f};
+        vx = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (key < Skv) {
+            kx = *reinterpret_cast<const f32x4*>(Kh + (size_t)key * D + 4 * c4);
+            vx = *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + 4 * c4);
+        }
+    };
+    auto store_vec = [&](int e, const f32x4& kx, const f32x4& vx) {
+        const int row = e / (D / 4);
+        const int c4 = e - row * (D / 4);
+        *reinterpret_cast<f32x4*>(&sK[row * KP + 4 * c4]) = kx;
+        *reinterpret_cast<f32x4*>(&sV[row * VP + 4 * c4]) = vx;
+    };
+    if constexpr (kPrefetch) {
+        if (kv_begin < kv_end) {
+#pragma unroll
+            for (int i = 0; i < PF; ++i) fetch_vec(kv_begin, tid + i * NT, kpf[i], vpf[i]);
+        }
+    }
+
     for (int kv0 = kv_begin; kv0 < kv_end; kv0 += BN) {
         __syncthreads();
-        for (int e = tid; e < BN * (D / 4); e += NT) {
-            const int row = e / (D / 4);
-            const int c4 = e - row * (D / 4);
-            const int key = kv0 + row;
-            f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-            if (key < Skv) {
-                kx = *reinterpret_cast<const f32x4*>(Kh + (size_t)key * D + 4 * c4);
-                vx = *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + 4 * c4);
+        if constexpr (kPrefetch) {
+#pragma unroll
+            for (int i = 0; i < PF; ++i) store_vec(tid + i * NT, kpf[i], vpf[i]);
+        } else {
+            for (int e = tid; e < NE; e += NT) {
+                f32x4 kx, vx;
+                fetch_vec(kv0, e, kx, vx);
+                store_vec(e, kx, vx);
             }
-            *reinterpret_cast<f32x4*>(&sK[row * KP + 4 * c4]) = kx;
-            *reinterpret_cast<f32x4*>(&sV[row * VP + 4 * c4]) = vx;
         }
         __syncthreads();
+        if constexpr (kPrefetch) {
+            if (kv0 + BN < kv_end) {
+#pragma unroll
+                for (int i = 0; i < PF; ++i) fetch_vec(kv0 + BN, tid + i * NT, kpf[i], vpf[i]);
+            }
+        }
 
         // scores s = scale * q.k in fp64, masked to -inf where invisible
         double s[NKB][4];
