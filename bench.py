@@ -196,23 +196,47 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` launches, HIP events around each on the launch stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    # timed region: exactly `steps` launches back to back, one HIP event pair
+    # around the region on the launch stream.  With --flush a scrub of the
+    # caches runs before every launch, so each launch gets its own events and
+    # the scrubs stay outside the timed intervals.
     scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev) if a.flush else None
+    if scrub is not None:
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    else:
+        region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.steps):
-        if scrub is not None:
+    if scrub is None:
+        region[0].record(stream)
+        for _ in range(a.steps):
+            step()
+        region[1].record(stream)
+    else:
+        for i in range(a.steps):
             scrub.fill_(float(i))
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_ms = sum(launch_ms) / len(launch_ms)
-    med_ms = sorted(launch_ms)[len(launch_ms) // 2]
+    if scrub is None:
+        avg_ms = region[0].elapsed_time(region[1]) / a.steps
+        # after the timed region: 31 launches, each bracketed by its own events
+        # (the events add their own overhead to every interval), for the median
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(31)]
+        for s0, s1 in pairs:
+            s0.record(stream)
+            step()
+            s1.record(stream)
+        torch.cuda.synchronize()
+        med_ms = sorted(s0.elapsed_time(s1) for s0, s1 in pairs)[15]
+    else:
+        launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        avg_ms = sum(launch_ms) / len(launch_ms)
+        med_ms = sorted(launch_ms)[len(launch_ms) // 2]
 
     flops = attention_flops(w.B, w.H, w.Sq, w.Skv, w.d, causal)
     # with --flush the wall clock also holds the scrubs: use the launch events
@@ -254,7 +278,8 @@ def main(argv=None) -> int:
                    "input_dist": w.dist, "seed": w.seed},
         "roofline": roofline,
     }
-    roofline.update({"launch_ms_avg": round(avg_ms, 5), "launch_ms_median": round(med_ms, 5),
+    roofline.update({"launch_ms_avg": round(avg_ms, 5),
+                     "launch_ms_median": None if med_ms is None else round(med_ms, 5),
                      "flops_per_launch": flops, "compulsory_bytes_per_launch": comp,
                      "compulsory_GBps": round(comp / (avg_ms * 1e-3) / 1e9, 1),
                      "hbm_peak_GBps": PEAK_HBM_GBS})
