@@ -651,9 +651,10 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                       acc[i][4 * r4 + 2] * inv, acc[i][4 * r4 + 3] * inv};
                     *reinterpret_cast<f32x4*>(part_o + prow * D + ch) = o4;
                 }
+            // (fp32 logarithm as in the unsplit LSE below, summed in fp64)
             if (h == 0)
                 part_lse[prow] =
-                    lt > 0.f ? ((double)m + log2((double)lt)) * (double)kLn2f : -INFINITY;
+                    lt > 0.f ? ((double)m + (double)log2f(lt)) * (double)kLn2f : -INFINITY;
         } else {
             const size_t obase = row * D;
 #pragma unroll
