@@ -159,7 +159,10 @@ def main(argv=None) -> int:
     dev = torch.device("cuda", 0)
     q_h, k_h, v_h = make_tensors(w)
     q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
-    tiles = tuple(int(x) for x in a.tiles.split("x")) if a.tiles else w.tiles
+    # the split path runs the selector's tiles: a workload's own forced tiles
+    # give way to them (only an explicit --tiles conflicts with --splits)
+    tiles = (tuple(int(x) for x in a.tiles.split("x")) if a.tiles
+             else (None if a.splits is not None else w.tiles))
     odt = q.dtype
     out = torch.empty(q.shape, dtype=odt, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)

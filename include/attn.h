@@ -157,10 +157,12 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * attn_select_splits -- the key-chunk count attn_fwd_split uses for
- * n_splits = 0 (host only, no HIP call): 1 when the query tiles alone give
- * every compute unit a workgroup, else enough chunks of whole key tiles to
- * do so (at most 64).  Writes the count and the chunk length in keys; either
- * pointer may be NULL.  Returns as attn_select_tiles.
+ * n_splits = 0 (host only, no HIP call): 1 when the query tiles alone reach
+ * the target, else enough chunks of whole key tiles to reach it (at most
+ * 64).  Target: one workgroup per compute unit for 16-bit inputs, four
+ * waves per compute unit (one per SIMD) for fp32.  Writes the count and the
+ * chunk length in keys; either pointer may be NULL.  Returns as
+ * attn_select_tiles.
  */
 int attn_select_splits(int d, int Sq, int Skv, int BH, int dtype, int causal,
                        int* n_splits, int* kv_chunk);

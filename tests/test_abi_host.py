@@ -164,6 +164,20 @@ def test_select_splits(lib, args, split):
         assert chunk % bn == 0 and (n - 1) * chunk < Skv <= n * chunk
 
 
+@pytest.mark.parametrize("args,want", [
+    # fp32: four waves per CU (1024 in all; a wave owns 16 query rows)
+    ((64, 512, 512, 8, B.F32, 0), (4, 128)),       # 256 one-wave query tiles
+    ((32, 1000, 1000, 6, B.F32, 1), (3, 384)),     # 378 one-wave query tiles
+    ((32, 8, 1000, 6, B.F32, 0), (16, 64)),        # capped by the 16 key tiles
+    ((64, 2048, 2048, 8, B.F32, 0), (1, 2048)),    # 256 four-wave query tiles already
+    # 16-bit: one workgroup per CU (256)
+    ((128, 1, 4000, 8, B.BF16, 0), (32, 128)),     # 8 tiles x 32 chunks of 4 key tiles
+    ((64, 512, 4096, 16, B.BF16, 0), (2, 2048)),   # 128 query tiles of 64 rows
+])
+def test_select_splits_counts(lib, args, want):
+    assert B.select_splits(*args) == want
+
+
 def _split(lib, n_splits=2, ws=0x600000, ws_bytes=1 << 20, **kw):
     # 1000 keys in 64-key tiles: two requested chunks do run, so each case
     # below fails validation before any HIP call
