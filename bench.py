@@ -127,7 +127,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="prefill_h32_s4096_d128")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 disables it)")
-    ap.add_argument("--tiles", default=None, help="force BMxBN, e.g. 128x64")
+    ap.add_argument("--tiles", default=None,
+                    help="force BMxBN, e.g. 128x64; 'auto' = the selector's tiles even "
+                         "where the workload forces its own")
     ap.add_argument("--splits", type=int, default=None,
                     help="time attn_fwd_split with this many key chunks (0 = library choice)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
@@ -161,8 +163,11 @@ def main(argv=None) -> int:
     q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
     # the split path runs the selector's tiles: a workload's own forced tiles
     # give way to them (only an explicit --tiles conflicts with --splits)
-    tiles = (tuple(int(x) for x in a.tiles.split("x")) if a.tiles
-             else (None if a.splits is not None else w.tiles))
+    if a.tiles == "auto":
+        tiles = None
+    else:
+        tiles = (tuple(int(x) for x in a.tiles.split("x")) if a.tiles
+                 else (None if a.splits is not None else w.tiles))
     odt = q.dtype
     out = torch.empty(q.shape, dtype=odt, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -250,7 +255,7 @@ def main(argv=None) -> int:
     in_b = 4 if dtype_name == "f32" else 2
     comp = compulsory_bytes(w.B, w.H, w.Sq, w.Skv, w.d, in_b, in_b)
     # counters were taken on the default launch (selector tiles, one key chunk, warm cache)
-    default_launch = a.tiles is None and n_splits is None and not a.flush
+    default_launch = tiles == w.tiles and n_splits is None and not a.flush
     traffic = measured_traffic(a.workload) if default_launch else None
 
     # bound: MFMA above the ridge point (peak FLOP/s over HBM bytes/s), HBM below

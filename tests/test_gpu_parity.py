@@ -167,6 +167,17 @@ def test_fp32_ragged_all_tiles(d, causal):
             check_full(q, k, v, causal, tiles=(bm, bn), what=f"fp32 77x133 d={d} ({bm},{bn})")
 
 
+@pytest.mark.parametrize("heads,kw", [(32, 2), (64, 1)], ids=["2 key waves", "1 key wave"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_key_waves_follow_the_grid(heads, kw, causal):
+    # forced 16 x 64 tiles on 17 query tiles per head: 544 query tiles give
+    # two waves per query block (each taking half of every key tile), 1088
+    # give one; small grids (above) give four
+    q, k, v = random_tensors(1, heads, 17 * 16 - 5, 200, 32, "f32", "normal", seed=31 + heads)
+    log(f"fp32 {heads} heads, {kw} key waves, causal={causal}")
+    check_full(q, k, v, causal, tiles=(16, 64), what=f"fp32 {heads} heads 16x64 kw={kw}")
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_empty_keys(dt):

@@ -145,7 +145,7 @@ int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
         while (bm > 16 && (wgs(bm) < kCUs || Sq <= bm / 2)) bm /= 2;
         t->block_m = bm;
         t->block_n = bn;
-        t->waves = bm / 16;
+        t->waves = bm / 16 * f32_key_waves(bm, bn, wgs(bm));
         t->lds_bytes = f32_lds_bytes(d, bm, bn);
         return ATTN_OK;
     }
@@ -278,6 +278,11 @@ int run(const Problem& p_in, int block_m, int block_n, int want_splits = -1,
                         block_n, p.d, p.dtype);
         t.block_m = block_m;
         t.block_n = block_n;
+        t.waves = p.dtype == ATTN_F32
+                      ? block_m / 16 *
+                            f32_key_waves(block_m, block_n,
+                                          bh * (long)((p.Sq + block_m - 1) / block_m))
+                      : block_m / 32;
     }
     hipError_t e;
     if (p.Skv == 0) {

@@ -4,7 +4,12 @@
 // score matrix" (section "Online normalization"), tiled over query rows and
 // key rows as in the tiled lab function of "Verify tiled attention".  Each
 // 64-wide wave owns 16 query rows; the workgroup's waves share one K/V tile
-// staged in LDS.
+// staged in LDS.  A workgroup has WQ x KW waves: WQ blocks of 16 query rows,
+// and KW waves per block that split every key tile among them (wave group
+// kg takes keys kg * BN/KW .. of each tile), each running the online softmax
+// over its own keys; at the end the KW states (m, l, a) of a row are merged
+// through LDS with the rescale rule applied to whole states.  KW > 1 fills
+// the SIMDs when the grid has few query tiles, with no workspace.
 //
 // Precision: scores are contracted on the fp64 matrix cores
 // (v_mfma_f64_16x16x4_f64).  Products of two fp32 numbers are exact in fp64,
@@ -33,19 +38,23 @@ namespace {
 
 constexpr double kLog2e = 1.4426950408889634074;
 
-template <int D, int BN, int WAVES, bool CAUSAL>
-__global__ __launch_bounds__(64 * WAVES)
+template <int D, int BN, int WQ, int KW, bool CAUSAL>
+__global__ __launch_bounds__(64 * WQ * KW)
 void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                          const float* __restrict__ V, float* __restrict__ O,
                          float* __restrict__ LSE, int n_bh, int Sq, int Skv, double scale,
                          int n_qt, int off, int kv_chunk, float* __restrict__ part_o,
                          double* __restrict__ part_lse) {
-    constexpr int BM = 16 * WAVES;
+    constexpr int WAVES = WQ * KW;
+    constexpr int BM = 16 * WQ;
     constexpr int NT = 64 * WAVES;
+    constexpr int KB = BN / KW;    // keys of a tile per wave
+    static_assert(KB % 16 == 0, "a wave takes whole 16-key blocks");
+    static_assert(KW == 1 || WQ == 1, "key-split workgroups hold one 16-row query block");
     constexpr int DQ = D / 4;      // head-dim quarter per lane group
     constexpr int KP = D + 4;      // K row pitch in floats: 16-byte reads of 8 rows spread over all banks
     constexpr int VP = D + 16;     // V row pitch: rows r and r+1 read by lanes 0-15 / 16-31 hit disjoint banks
-    constexpr int NKB = BN / 16;   // 16-key blocks per tile
+    constexpr int NKB = KB / 16;   // 16-key blocks per tile and wave
     constexpr int ND = D / 16;     // 16-wide output channel blocks
     __shared__ __attribute__((aligned(16))) float sK[BN * KP];
     __shared__ __attribute__((aligned(16))) float sV[BN * VP];
@@ -55,9 +64,12 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wq = wave % WQ;      // query block of the wave
+    const int kg = wave / WQ;      // key group of the wave
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int qi = qt * BM + wave * 16 + c;
+    const int qi = qt * BM + wq * 16 + c;
+    const int kw0 = kg * KB;       // first key of a tile this wave takes
 
     const float* Qh = Q + (size_t)bh * Sq * D;
     const float* Kh = K + (size_t)bh * Skv * D;
@@ -151,7 +163,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f64x4 st = {0.0, 0.0, 0.0, 0.0};
-            const float* krow = &sK[(kb * 16 + c) * KP + g * DQ];
+            const float* krow = &sK[(kw0 + kb * 16 + c) * KP + g * DQ];
 #pragma unroll
             for (int t = 0; t < DQ; t += 4) {
                 f32x4 kx = *reinterpret_cast<const f32x4*>(krow + t);
@@ -162,7 +174,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int j = kv0 + kb * 16 + g + 4 * r;
+                const int j = kv0 + kw0 + kb * 16 + g + 4 * r;
                 const bool vis = (j < Skv) && (!CAUSAL || j <= qi + off);
                 s[kb][r] = vis ? st[r] * scale : -INFINITY;
             }
@@ -200,7 +212,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float* vrow = &sV[(kb * 16 + g + 4 * r) * VP + c];
+                const float* vrow = &sV[(kw0 + kb * 16 + g + 4 * r) * VP + c];
 #pragma unroll
                 for (int i = 0; i < ND; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * i], p[kb][r], acc[i],
@@ -211,6 +223,43 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     // O = a / l, LSE = m + ln l; rows that saw no key keep O = 0, LSE = -inf
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
+    if constexpr (KW > 1) {
+        // Merge the key groups' states of each row: M = max_k m_k,
+        // w_k = e^(m_k - M) (0 for a group that saw no key), l = sum w_k l_k,
+        // a = sum w_k a_k.  The tile buffers are free once every wave has
+        // finished its last tile.
+        static_assert(KW * 16 * D <= BN * KP, "merged accumulators fit the K buffer");
+        static_assert(KW * 16 * 12 <= BN * VP * 4, "row states fit the V buffer");
+        float* red_a = sK;                                         // [KW][16][D]
+        double* red_m = reinterpret_cast<double*>(sV);             // [KW][16]
+        float* red_l = sV + 2 * KW * 16;                           // [KW][16]
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+            *reinterpret_cast<f32x4*>(&red_a[(kg * 16 + c) * D + 16 * i + 4 * g]) = acc[i];
+        if (g == 0) {
+            red_m[kg * 16 + c] = m;
+            red_l[kg * 16 + c] = lt;
+        }
+        __syncthreads();
+        if (kg != 0) return;       // key group 0 finishes the rows
+        double M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) M = fmax(M, red_m[k * 16 + c]);
+        lt = 0.f;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+            const double mk = red_m[k * 16 + c];
+            const float w = mk == -INFINITY ? 0.f : exp2f((float)((mk - M) * kLog2e));
+            lt += w * red_l[k * 16 + c];
+#pragma unroll
+            for (int i = 0; i < ND; ++i)
+                acc[i] += w * *reinterpret_cast<const f32x4*>(&red_a[(k * 16 + c) * D + 16 * i + 4 * g]);
+        }
+        m = M;
+    }
     if (qi < Sq) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const double lse = lt > 0.f ? m + log((double)lt) : -INFINITY;
@@ -233,45 +282,55 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     }
 }
 
-template <int D, int BN, int WAVES>
+template <int D, int BN, int WQ, int KW>
 hipError_t launch_one(const Problem& p) {
-    constexpr int BM = 16 * WAVES;
+    constexpr int BM = 16 * WQ;
     const int n_bh = p.B * p.H;
     const int n_qt = (p.Sq + BM - 1) / BM;
     const dim3 grid((unsigned)(n_bh * n_qt), (unsigned)p.n_splits);
-    const dim3 block(64 * WAVES);
+    const dim3 block(64 * WQ * KW);
     const double scale = (double)p.scale;
     const float* q = static_cast<const float*>(p.q);
     const float* k = static_cast<const float*>(p.k);
     const float* v = static_cast<const float*>(p.v);
     float* o = static_cast<float*>(p.o);
     if (p.causal)
-        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, true>), grid, block, 0, p.stream,
+        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WQ, KW, true>), grid, block, 0, p.stream,
                            q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.causal_off, p.kv_chunk,
                            p.part_o, p.part_lse);
     else
-        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WAVES, false>), grid, block, 0, p.stream,
+        hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WQ, KW, false>), grid, block, 0, p.stream,
                            q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.causal_off, p.kv_chunk,
                            p.part_o, p.part_lse);
     return hipGetLastError();
 }
 
 template <int D, int BN>
-hipError_t by_waves(const Problem& p, int waves) {
-    switch (waves) {
-        case 1: return launch_one<D, BN, 1>(p);
-        case 2: return launch_one<D, BN, 2>(p);
-        case 4: return launch_one<D, BN, 4>(p);
-        default: return hipErrorInvalidValue;
+hipError_t by_waves(const Problem& p, int wq, int kw) {
+    if (kw == 1) {
+        switch (wq) {
+            case 1: return launch_one<D, BN, 1, 1>(p);
+            case 2: return launch_one<D, BN, 2, 1>(p);
+            case 4: return launch_one<D, BN, 4, 1>(p);
+            default: return hipErrorInvalidValue;
+        }
     }
+    if (wq != 1) return hipErrorInvalidValue;
+    if constexpr (BN >= 32) {
+        if (kw == 2) return launch_one<D, BN, 1, 2>(p);
+    }
+    if constexpr (BN >= 64) {
+        if (kw == 4) return launch_one<D, BN, 1, 4>(p);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t by_bn(const Problem& p, int bn, int waves) {
+hipError_t by_bn(const Problem& p, int bn, int wq, int kw) {
     switch (bn) {
-        case 16: return by_waves<D, 16>(p, waves);
-        case 32: return by_waves<D, 32>(p, waves);
-        case 64: return by_waves<D, 64>(p, waves);
+        case 16: return by_waves<D, 16>(p, wq, kw);
+        case 32: return by_waves<D, 32>(p, wq, kw);
+        case 64: return by_waves<D, 64>(p, wq, kw);
         default: return hipErrorInvalidValue;
     }
 }
@@ -289,14 +348,22 @@ int f32_lds_bytes(int d, int /*block_m*/, int block_n) {
     return block_n * ((d + 4) + (d + 16)) * (int)sizeof(float);
 }
 
+int f32_key_waves(int block_m, int block_n, long query_tiles) {
+    if (block_m != 16) return 1;
+    const int kw = query_tiles >= 1024 ? 1 : (query_tiles >= 512 ? 2 : 4);
+    return kw < block_n / 16 ? kw : block_n / 16;
+}
+
 hipError_t launch_f32(const Problem& p, const Tiles& t) {
     if (!f32_tiles_supported(p.d, t.block_m, t.block_n)) return hipErrorInvalidValue;
-    const int waves = t.block_m / 16;
+    const int wq = t.block_m / 16;
+    const long n_qt = (p.Sq + t.block_m - 1) / t.block_m;
+    const int kw = f32_key_waves(t.block_m, t.block_n, (long)p.B * p.H * n_qt);
     switch (p.d) {
-        case 16: return by_bn<16>(p, t.block_n, waves);
-        case 32: return by_bn<32>(p, t.block_n, waves);
-        case 64: return by_bn<64>(p, t.block_n, waves);
-        case 128: return by_bn<128>(p, t.block_n, waves);
+        case 16: return by_bn<16>(p, t.block_n, wq, kw);
+        case 32: return by_bn<32>(p, t.block_n, wq, kw);
+        case 64: return by_bn<64>(p, t.block_n, wq, kw);
+        case 128: return by_bn<128>(p, t.block_n, wq, kw);
         default: return hipErrorInvalidValue;
     }
 }
