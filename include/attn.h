@@ -116,8 +116,12 @@ int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* 
  * attn_select_tiles -- the tile / occupancy selector (host only, no HIP
  * call).  Writes the tile shape attn_fwd would use for this problem:
  * query rows per workgroup, key rows per tile, 64-wide waves per workgroup
- * and LDS bytes per workgroup.  `BH` is B * H.  Any output pointer may be
- * NULL.  Returns ATTN_OK, ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED.
+ * and LDS bytes per workgroup.  fp32 waves own 16 query rows each; with
+ * 16-row query tiles on a grid of fewer than 512 (1024) query tiles, four
+ * (two) waves share each 16-row block, each taking its part of every key
+ * tile, and merge their states at the end (at most block_n / 16 waves).
+ * `BH` is B * H.  Any output pointer may be NULL.  Returns ATTN_OK,
+ * ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED.
  */
 int attn_select_tiles(int d, int Sq, int Skv, int BH, int dtype, int causal,
                       int* block_m, int* block_n, int* waves, int* lds_bytes);
