@@ -5,8 +5,8 @@
 // score matrix" (section "Online normalization") over query tiles and key
 // tiles as in the tiled lab function of "Verify tiled attention".  Each
 // 64-wide wave owns 32 query rows; the waves of a workgroup share one K/V
-// tile staged in LDS.  K/V tiles travel HBM -> LDS by DMA two steps ahead
-// of their use, so the loads overlap with the MFMA work.
+// tile staged in LDS.  K/V tiles travel HBM -> LDS by DMA well ahead of their
+// use, so the loads overlap with the MFMA work.
 //
 // Contractions use v_mfma_f32_32x32x16_bf16 / _f16 (A 32x16, B 16x32, D 32x32):
 //   lane = 32 h + c (h in 0..1, c in 0..31);
@@ -170,13 +170,16 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c, int,
 // S_{j+1} = K_{j+1} Q^T and add P_{j-1} V_{j-1} to the accumulator, the two
 // kinds of MFMA alternating, while the VALU runs the online-softmax update
 // of S_j between them (row max, reference and rescale factor, exponentials,
-// row sums, packing into P_j).  K and V live in three LDS buffers each (K_t
-// in sK[t % 3], V_t in sV[t % 3]); step j starts the DMA of K_{j+3} and
-// V_{j+1} into the buffers its predecessor finished reading and ends with one
-// workgroup barrier after waiting for the DMA issued one step earlier.  The
-// instruction order is fixed by hand (sched_barrier fences): every MFMA
-// operand is read from LDS two MFMAs ahead of its use, and the VALU work is
-// cut into slices placed between consecutive MFMAs.
+// row sums, packing into P_j).  K and V live in four LDS buffers each (K_t
+// in sK[t % 4], V_t in sV[t % 4]); step j starts the DMA of K_{j+4} and
+// V_{j+2} into the buffers its predecessor finished reading and ends with one
+// workgroup barrier after waiting for the DMA issued one step earlier, so
+// the tiles step j + 1 reads (K_{j+2}, V_j) are already visible during step
+// j.  The instruction order is fixed by hand (sched_barrier fences): every
+// MFMA operand is read from LDS two MFMAs ahead of its use, across step
+// boundaries too (the last MFMAs of step j read the first operands of step
+// j + 1 before the barrier), and the VALU work is cut into slices placed
+// between consecutive MFMAs.
 template <typename T, int D, int BN, int WAVES, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
@@ -203,20 +206,22 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     static_assert(DCH == 8 || DCH == 16, "K swizzle covers 8 or 16 chunks per row");
     static_assert(NA >= 4 && NB >= ND + 1, "schedule needs a few MFMAs per phase");
 
-    // Three buffers each for K and V: K_t lives in sK[t % 3], V_t in
-    // sV[t % 3], and tiles are fetched two steps ahead of their use.
-    // Separate arrays (not one indexed at run time) let the compiler see that
-    // the DMA into one buffer never aliases reads of another.
+    // Four buffers each for K and V: K_t lives in sK[t % 4], V_t in
+    // sV[t % 4].  Separate arrays (not one indexed at run time) let the
+    // compiler see that the DMA into one buffer never aliases reads of
+    // another.
     __shared__ __attribute__((aligned(16))) T sK0[BN * D];
     __shared__ __attribute__((aligned(16))) T sK1[BN * D];
     __shared__ __attribute__((aligned(16))) T sK2[BN * D];
+    __shared__ __attribute__((aligned(16))) T sK3[BN * D];
     __shared__ __attribute__((aligned(16))) T sV0[BN * D];
     __shared__ __attribute__((aligned(16))) T sV1[BN * D];
     __shared__ __attribute__((aligned(16))) T sV2[BN * D];
+    __shared__ __attribute__((aligned(16))) T sV3[BN * D];
     __shared__ int s_vote[WAVES];      // per-wave vote of the fast pass
     // vmcnt value that leaves exactly one step's DMA (K and V) in flight
     constexpr int kWaitOlderDma = wait_vmcnt(2 * PER);
-    static_assert(3 * PER < 64, "DMA counts must fit the 6-bit vmcnt field");
+    static_assert(5 * PER < 64, "DMA counts must fit the 6-bit vmcnt field");
 
     // K layout in LDS: unpadded rows of DCH 16-byte chunks; chunk q of row r
     // sits at position q ^ k_swz(r).  An operand read (16 lanes = 16
@@ -369,25 +374,31 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // moves the accumulator to a new reference only after the P.V MFMAs,
     // and only when some row of the wave raised it; the other tiles take
     // their exponentials against the current reference from the first slot.
-    auto fused = [&](auto QK, auto PV, auto EX, const T* __restrict__ sk,
+    // The first two K and V operands arrive in kp / vp, read during the
+    // previous step; with PF the step reads those of the next step from
+    // sk_pre / sv_pre in their place.
+    auto fused = [&](auto QK, auto PV, auto EX, auto PF, const T* __restrict__ sk,
                      const T* __restrict__ sv, const f32x16* st, f32x16* sn,
-                     const V8 (*po)[2], V8 (*pn)[2]) __attribute__((always_inline)) {
+                     const V8 (*po)[2], V8 (*pn)[2], V8* kp, V8* vp,
+                     const T* __restrict__ sk_pre,
+                     const T* __restrict__ sv_pre) __attribute__((always_inline)) {
         constexpr bool qk = decltype(QK)::value;
         constexpr bool pv = decltype(PV)::value;
         constexpr bool ex_max = decltype(EX)::value;
+        constexpr bool pf = decltype(PF)::value;
         constexpr int NM = (qk ? NA : 0) + (pv ? NB : 0);   // MFMAs of the step
         constexpr int NS = NM > 4 ? NM : 4;                  // schedule slots
         constexpr int S0 = ex_max ? 2 : 0;                   // first slot with exponentials
         V8 ka[3], va[3];
         if constexpr (qk) {
-            ka[0] = k_operand(sk, 0);
-            ka[1] = k_operand(sk, 1);
+            ka[0] = kp[0];
+            ka[1] = kp[1];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) sn[kb] = f32x16{};
         }
         if constexpr (pv) {
-            va[0] = v_operand(sv, 0);
-            va[1] = v_operand(sv, 1);
+            va[0] = vp[0];
+            va[1] = vp[1];
         }
         float mx = -INFINITY, alpha = 1.f, psum = 0.f;
         bool rescale = false;
@@ -423,10 +434,12 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 // no MFMA in this slot
             } else if (is_qk) {
                 if (t + 2 < NA) ka[(t + 2) % 3] = k_operand(sk, t + 2);
+                else if (pf) kp[t + 2 - NA] = k_operand(sk_pre, t + 2 - NA);
                 const int kb = t % NKB, ks = t / NKB;
                 sn[kb] = mfma_32x32x16(ka[t % 3], qop[ks], sn[kb], 0, 0, 0);
             } else {
                 if (t + 2 < NB) va[(t + 2) % 3] = v_operand(sv, t + 2);
+                else if (pf) vp[t + 2 - NB] = v_operand(sv_pre, t + 2 - NB);
                 const int u = t / ND, i = t % ND;
                 acc[i] = mfma_32x32x16(va[t % 3], po[u / 2][u % 2],
                                                                  acc[i], 0, 0, 0);
@@ -466,6 +479,11 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
+        if constexpr (pf && !pv) {
+            // (the first step has no P.V to carry the V prefetch)
+            vp[0] = v_operand(sv_pre, 0);
+            vp[1] = v_operand(sv_pre, 1);
+        }
         sum_pack((NS - S0 - 1) * NV / (NS - S0), NV);     // the last slot's values
         if constexpr (ex_max) {
             l = l * alpha + psum;
@@ -504,28 +522,30 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     using T_ = integral_constant<bool, true>;
     using F_ = integral_constant<bool, false>;
     // Steady-state step j: scores of tile j + 1, P.V of tile j - 1, softmax
-    // of tile j; DMA of K_{j+3} and V_{j+1}.  The buffers arrive as distinct
-    // restrict pointers: once inlined, every LDS access and DMA in the step
-    // carries scoped no-alias metadata, which lets the compiler see that the
-    // DMA into the free buffers never overlaps the operand reads of the busy
-    // ones (the transposing read otherwise waits for all DMA in flight).
-    auto step = [&](auto PV, auto EX, int j, f32x16* st, V8 (*po)[2],
-                    const T* __restrict__ k_next, T* __restrict__ k_free,
-                    const T* __restrict__ v_prev, T* __restrict__ v_free) {
+    // of tile j; DMA of K_{j+4} and V_{j+2}; first operands of step j + 1
+    // from K_{j+2} and V_j.  The buffers arrive as distinct restrict
+    // pointers: once inlined, every LDS access and DMA in the step carries
+    // scoped no-alias metadata, which lets the compiler see that the DMA into
+    // the free buffers never overlaps the operand reads of the busy ones (the
+    // transposing read otherwise waits for all DMA in flight).
+    auto step = [&](auto PV, auto EX, int j, f32x16* st, V8 (*po)[2], V8* kp, V8* vp,
+                    const T* __restrict__ k_next, const T* __restrict__ k_pre,
+                    T* __restrict__ k_free, const T* __restrict__ v_prev,
+                    const T* __restrict__ v_pre, T* __restrict__ v_free) {
         const int kv0 = kv_begin + j * BN;
-        load_k(kv0 + 3 * BN, k_free);           // K_{j+3}: zero rows or unused past the end
-        load_v(kv0 + BN, v_free);               // V_{j+1}
+        load_k(kv0 + 4 * BN, k_free);           // K_{j+4}: zero rows or unused past the end
+        load_v(kv0 + 2 * BN, v_free);           // V_{j+2}
         mask(kv0, st);
         f32x16 sn[NKB];
         V8 pn[NKB][2];
-        fused(T_{}, PV, EX, k_next, v_prev, st, sn, po, pn);
+        fused(T_{}, PV, EX, T_{}, k_next, v_prev, st, sn, po, pn, kp, vp, k_pre, v_pre);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             st[kb] = sn[kb];
             po[kb][0] = pn[kb][0];
             po[kb][1] = pn[kb][1];
         }
-        __builtin_amdgcn_s_waitcnt(kWaitOlderDma);   // K_{j+2}, V_j have landed
+        __builtin_amdgcn_s_waitcnt(kWaitOlderDma);   // K_{j+3}, V_{j+1} have landed
         ring_barrier();
     };
 
@@ -560,12 +580,14 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     }
 
     if (n_tiles > 0) {
-        // ---- prologue: K_0, K_1, V_0, K_2 in flight; S_0 from K_0 ----
+        // ---- prologue: K_0 .. K_3, V_0, V_1 in flight; S_0 from K_0 ----
         load_k(kv_begin, sK0);
         load_k(kv_begin + BN, sK1);
-        load_v(kv_begin, sV0);
         load_k(kv_begin + 2 * BN, sK2);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * PER));   // K_0 has landed
+        load_v(kv_begin, sV0);
+        load_k(kv_begin + 3 * BN, sK3);
+        load_v(kv_begin + BN, sV1);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(5 * PER));   // K_0 has landed
         ring_barrier();
         f32x16 st[NKB];
 #pragma unroll
@@ -576,45 +598,58 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 st[kb] = mfma_32x32x16(k_operand(sK0, ks * NKB + kb),
                                                                  qop[ks], st[kb], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER));   // K_1 has landed
+        // K_1, K_2 and V_0 have landed: step 0 reads K_1 and, for step 1,
+        // K_2 and V_0
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * PER));
         ring_barrier();
 
         // ---- steps 0 .. n_tiles - 2 (each has a next tile) ----
-        // buffers of step j: K_{j+1}, free slot of K_j, V_{j-1}, free slot of V_{j-2}
+        // buffers of step j: K_{j+1}, K_{j+2}, free slot of K_j, V_{j-1},
+        // V_j, free slot of V_{j-2}
         V8 po[NKB][2];      // probabilities of the previous tile
+        V8 kp[2], vp[2];    // first two K and V operands of the next step
+        kp[0] = k_operand(sK1, 0);
+        kp[1] = k_operand(sK1, 1);
         int j = 0;
         if (n_tiles > 1) {
             // no P.V yet; the row maximum sets the reference of either pass
-            step(F_{}, T_{}, 0, st, po, sK1, sK0, sV2, sV1);
+            step(F_{}, T_{}, 0, st, po, kp, vp, sK1, sK2, sK0, sV3, sV0, sV2);
             j = 1;
-            for (; j + 3 < n_tiles; j += 3) {
-                step(T_{}, F_{}, j, st, po, sK2, sK1, sV0, sV2);
-                step(T_{}, F_{}, j + 1, st, po, sK0, sK2, sV1, sV0);
-                step(T_{}, F_{}, j + 2, st, po, sK1, sK0, sV2, sV1);
+            for (; j + 4 < n_tiles; j += 4) {
+                step(T_{}, F_{}, j, st, po, kp, vp, sK2, sK3, sK1, sV0, sV1, sV3);
+                step(T_{}, F_{}, j + 1, st, po, kp, vp, sK3, sK0, sK2, sV1, sV2, sV0);
+                step(T_{}, F_{}, j + 2, st, po, kp, vp, sK0, sK1, sK3, sV2, sV3, sV1);
+                step(T_{}, F_{}, j + 3, st, po, kp, vp, sK1, sK2, sK0, sV3, sV0, sV2);
             }
-            if (j + 1 < n_tiles) {               // j % 3 == 1 here
-                step(T_{}, F_{}, j, st, po, sK2, sK1, sV0, sV2);
+            if (j + 1 < n_tiles) {               // j % 4 == 1 here
+                step(T_{}, F_{}, j, st, po, kp, vp, sK2, sK3, sK1, sV0, sV1, sV3);
                 ++j;
             }
             if (j + 1 < n_tiles) {
-                step(T_{}, F_{}, j, st, po, sK0, sK2, sV1, sV0);
+                step(T_{}, F_{}, j, st, po, kp, vp, sK3, sK0, sK2, sV1, sV2, sV0);
+                ++j;
+            }
+            if (j + 1 < n_tiles) {
+                step(T_{}, F_{}, j, st, po, kp, vp, sK0, sK1, sK3, sV2, sV3, sV1);
                 ++j;
             }
         }
-        // ---- last tile j = n_tiles - 1: P.V of tile j - 1, softmax of
-        // tile j, then its P.V.  All DMA has landed first (also what the
-        // next query tile needs).
+        // ---- last tile j = n_tiles - 1: P.V of tile j - 1 (its first
+        // operands in vp), softmax of tile j, then its P.V.  All DMA has
+        // landed first (also what the next query tile needs).
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
-        const int r = j % 3;
-        const T* v_prev = r == 0 ? sV2 : (r == 1 ? sV0 : sV1);
-        const T* v_last = r == 0 ? sV0 : (r == 1 ? sV1 : sV2);
+        const int r = j % 4;
+        const T* v_last = r == 0 ? sV0 : (r == 1 ? sV1 : (r == 2 ? sV2 : sV3));
+        const T* v_prev = r == 0 ? sV3 : (r == 1 ? sV0 : (r == 2 ? sV1 : sV2));
         mask(kv_begin + j * BN, st);
         V8 pn[NKB][2];
         if (j > 0)
-            fused(F_{}, T_{}, F_{}, nullptr, v_prev, st, nullptr, po, pn);
+            fused(F_{}, T_{}, F_{}, F_{}, nullptr, v_prev, st, nullptr, po, pn, kp, vp, nullptr,
+                  nullptr);
         else
-            fused(F_{}, F_{}, T_{}, nullptr, nullptr, st, nullptr, po, pn);
+            fused(F_{}, F_{}, T_{}, F_{}, nullptr, nullptr, st, nullptr, po, pn, kp, vp, nullptr,
+                  nullptr);
         pv_tile(v_last, pn);
     }
 
@@ -740,7 +775,7 @@ bool bf16_tiles_supported(int d, int block_m, int block_n) {
 }
 
 int bf16_lds_bytes(int d, int /*block_m*/, int block_n) {
-    return 3 * 2 * block_n * d * 2;   // K and V, three buffers each
+    return 4 * 2 * block_n * d * 2;   // K and V, four buffers each
 }
 
 namespace {
