@@ -281,6 +281,15 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         }
     };
 
+    // Byte offset of this lane's K operand (row c, chunk 2 ks + h) within a K
+    // buffer, per k-step of the score contraction.
+    int koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        koff[ks] = c * ROWB + 16 * ((2 * ks + h) ^ k_swz(c));
+        pin(koff[ks]);
+    }
+
     // ---- one query tile: Q operand, online softmax over its key tiles, O/LSE ----
     // preset: take the rows' maxima over all key tiles first and start from
     // them (no vote); otherwise the first tile's maxima, then the vote.
@@ -326,10 +335,14 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // ---- operand reads ----
     // K operand of score MFMA t: key block kb = t % NKB, k-step ks = t / NKB
     // (the accumulators of the key blocks alternate)
+    // (the swizzle of row kb * 32 + c equals that of row c, so key block kb
+    // only adds a constant; kept opaque, the lane's byte offset per k-step
+    // is one register and the buffer and key block fold into the read's
+    // immediate offset)
     auto k_operand = [&](const T* sk, int t) -> V8 {
         const int kb = t % NKB, ks = t / NKB;
-        const int row = kb * 32 + c;
-        return *reinterpret_cast<const V8*>(sk + row * D + 8 * ((2 * ks + h) ^ k_swz(row)));
+        return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(sk) +
+                                            kb * 32 * ROWB + koff[ks]);
     };
     // V operand of P.V MFMA t: k-step s = t / ND (keys 16 s .. 16 s + 15),
     // channel block i = t % ND; two transposing reads, keys 8 h + 4 u .. + 3
