@@ -27,7 +27,8 @@ def test_f16_ragged_tiles(d, causal, tiles):
 
 
 def test_f16_every_tile_count():
-    for n in range(1, 8):
+    # 1 .. 10 key tiles: every trip count and remainder of the tile loop
+    for n in range(1, 11):
         for skv in sorted({(n - 1) * 32 + 1, n * 32}):
             q, k, v = random_tensors(1, 2, 70, skv, 128, "f16", "normal", seed=2000 + skv)
             for causal in (False, True):

@@ -144,12 +144,13 @@ def test_bf16_ragged_tiles(d, causal, tiles):
 
 @pytest.mark.parametrize("tiles", [(128, 32), (64, 64), (256, 32)], ids=["128x32", "64x64", "256x32"])
 def test_bf16_every_tile_count(tiles):
-    # key lengths giving 1 .. 7 key tiles, full and ragged, so that every
-    # entry and exit of the pipelined tile loop runs (no next tile, one, two,
-    # three-step trips with each remainder)
+    # key lengths giving 1 .. 10 key tiles, full and ragged, so that every
+    # entry and exit of the pipelined tile loop runs: no next tile, the
+    # four-step unrolled loop run zero, one or two times, and every remainder
+    # of zero to three steps after it
     d = 128
     bn = tiles[1]
-    for n in range(1, 8):
+    for n in range(1, 11):
         for skv in sorted({(n - 1) * bn + 1, n * bn}):
             q, k, v = random_tensors(1, 2, 70, skv, d, "bf16", "normal", seed=1000 + skv)
             log(f"bf16 tile count {n} Skv={skv} tiles={tiles}")
