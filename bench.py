@@ -17,7 +17,10 @@ fp64 oracle timed on a bounded sample of the same workload on the host).
 
 ``--copy-probe BYTES`` instead times a plain device-to-device copy of BYTES
 bytes; its rocprofv3 FETCH_SIZE / WRITE_SIZE readings calibrate the HBM
-counters against a transfer of known size.
+counters against a transfer of known size.  ``--gemm-probe N`` times a
+dense N x N x N bf16 torch.matmul on random and on all-zero operands (the
+chip's matrix-core rate under its power limit, for data that toggle like
+the benchmark's and for data that do not).
 """
 from __future__ import annotations
 
@@ -129,6 +132,39 @@ def copy_probe(nbytes: int, steps: int) -> None:
     print(json.dumps({"copy_probe_bytes": nbytes, "steps": steps}), flush=True)
 
 
+def gemm_probe(n: int, steps: int) -> None:
+    """Dense bf16 GEMM rate (torch.matmul, n x n x n) on random and on all-zero
+    operands: the same instructions, different bit toggling.  Under a power
+    limit the random-operand rate is the attainable matrix-core rate for
+    data like the benchmark's."""
+    import torch
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    res = {"gemm_probe": n, "steps": steps, "dtype": "bf16"}
+    for name in ("random", "zeros"):
+        if name == "random":
+            a = (torch.rand(n, n, generator=g) * 1.6 - 0.8).to(torch.bfloat16).to(dev)
+            b = (torch.rand(n, n, generator=g) * 1.6 - 0.8).to(torch.bfloat16).to(dev)
+        else:
+            a = torch.zeros(n, n, dtype=torch.bfloat16, device=dev)
+            b = torch.zeros(n, n, dtype=torch.bfloat16, device=dev)
+        c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+        for _ in range(max(3, steps // 4)):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    print(json.dumps(res), flush=True)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +181,11 @@ def main(argv=None) -> int:
     ap.add_argument("--splits", type=int, default=None,
                     help="time attn_fwd_split with this many key chunks (0 = library choice)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--zero-inputs", action="store_true",
+                    help="diagnostic: all-zero Q, K, V of the workload's shape (same instructions, "
+                         "no operand bit toggling); not the benchmark")
+    ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
+                    help="time an N x N x N bf16 torch.matmul on random and on zero operands")
     ap.add_argument("--flush", action="store_true",
                     help="overwrite a 1 GiB buffer before each timed launch (outside the "
                          "per-launch events), so K/V start outside L2 and Infinity Cache; "
@@ -163,6 +204,9 @@ def main(argv=None) -> int:
     if a.copy_probe:
         copy_probe(a.copy_probe, max(1, a.steps))
         return 0
+    if a.gemm_probe:
+        gemm_probe(a.gemm_probe, max(1, a.steps))
+        return 0
 
     from seeded_inputs import WORKLOADS, make_tensors
     from tiled_online_softmax_05_amd import binding
@@ -172,6 +216,10 @@ def main(argv=None) -> int:
     causal = True in w.causal_modes
     dev = torch.device("cuda", 0)
     q_h, k_h, v_h = make_tensors(w)
+    if a.zero_inputs:
+        # diagnostic: the same launches on operands that do not toggle
+        q_h, k_h, v_h = (torch.zeros_like(x) for x in (q_h, k_h, v_h))
+        a.cpu_budget = 0
     q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
     # the split path runs the selector's tiles: a workload's own forced tiles
     # give way to them (only an explicit --tiles conflicts with --splits)
@@ -295,7 +343,7 @@ def main(argv=None) -> int:
         "config": {"workload": a.workload, "B": w.B, "H": w.H, "Sq": w.Sq, "Skv": w.Skv,
                    "d": w.d, "causal": causal, "tiles": list(tiles_used),
                    "key_chunks": n_splits or 1, "cache": "flushed" if a.flush else "warm",
-                   "input_dist": w.dist, "seed": w.seed},
+                   "input_dist": "zeros" if a.zero_inputs else w.dist, "seed": w.seed},
         "roofline": roofline,
     }
     roofline.update({"launch_ms_avg": round(avg_ms, 5),
