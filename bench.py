@@ -86,9 +86,13 @@ def cpu_baseline(q, k, v, causal: bool, budget_s: float) -> dict:
     import oracle
     from seeded_inputs import to_f64
     from tiled_online_softmax_05_amd.accounting import attention_flops
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+                         for i in info if i.get("user_api") == "blas") or "none loaded"
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = os.cpu_count() or 1
     _, H, Sq, d = q.shape
@@ -115,6 +119,7 @@ def cpu_baseline(q, k, v, causal: bool, budget_s: float) -> dict:
     how = (f"median of {len(rates)} passes over {H} heads" if done == H
            else f"{done} of {H} heads")
     return {"value": round(value / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "blas": blas,
             "kind": "oracle",
             "sample": f"{how} (B=1, Sq={Sq}, Skv={Skv}, d={d}, causal={causal}), fp64 numpy "
                       f"direct attention, {dt:.1f} s"}
