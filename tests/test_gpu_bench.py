@@ -1,0 +1,49 @@
+"""bench.py's output line on the GPU: the fields the benchmark contract names,
+for the headline workload and for an HBM-bound small one."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+pytestmark = pytest.mark.gpu
+
+
+def run_bench(*args):
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return json.loads(lines[0])
+
+
+def test_headline_line_has_the_contract_fields():
+    rec = run_bench("--steps", "5", "--warmup", "5", "--cpu-budget", "0.5")
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in rec, key
+    assert rec["n_gpus"] == 1 and rec["steps"] == 5 and rec["warmup"] == 5
+    assert rec["unit"] == "TFLOP/s" and rec["dtype"] == "bf16" and rec["higher_is_better"]
+    assert rec["config"]["workload"] == "prefill_h32_s4096_d128"
+    assert rec["value"] > 0
+    ro = rec["roofline"]
+    assert ro["bound"] == "mfma" and ro["unit"] == "TFLOP/s" and ro["peak"] == 2516.6
+    assert 0 < ro["frac"] < 1 and abs(ro["frac"] - ro["achieved"] / ro["peak"]) < 1e-3
+    assert ro["flops_per_launch"] == 4 * 32 * 4096 * 4096 * 128 / 2
+    assert ro["traffic"] is None or ro["traffic"] > ro["compulsory_bytes_per_launch"] * 0.9
+    cb = rec["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
+    assert cb["cores"] >= 1 and cb["sample"]
+
+
+def test_hbm_bound_workload_reports_bandwidth():
+    rec = run_bench("--workload", "stress_b3h2_d32_skv1000", "--splits", "0",
+                    "--steps", "5", "--warmup", "5", "--cpu-budget", "0")
+    ro = rec["roofline"]
+    assert ro["bound"] == "hbm" and ro["unit"] == "GB/s" and ro["peak"] == 8000.0
+    assert rec["config"]["key_chunks"] > 1
+    assert "cpu_baseline" not in rec
