@@ -127,6 +127,23 @@ def test_longctx_h64_s32768_d128_sampled(longctx, out_dtype):
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------------------------ other full-size 16-bit shapes
+@pytest.mark.parametrize("B_,H,Sq,Skv,d,causal,dist", [
+    (1, 32, 4096, 4096, 64, True, "normal"),          # d = 64 at the headline size
+    (1, 16, 4096, 4096, 128, False, "uniform0.8"),    # non-causal, every key tile of every row
+    (2, 8, 1024, 8192, 128, True, "normal"),          # prefill after a key cache (end-aligned)
+], ids=["d64_causal_s4096", "d128_noncausal_s4096", "sq1024_skv8192_causal"])
+def test_bf16_full_size_sampled(B_, H, Sq, Skv, d, causal, dist):
+    q, k, v = random_tensors(B_, H, Sq, Skv, d, "bf16", dist, seed=Sq + Skv + d)
+    log(f"bf16 full size B={B_} H={H} Sq={Sq} Skv={Skv} d={d} causal={causal} {dist}")
+    o, lse = gpu_run(q, k, v, causal, out_dtype=torch.float32)
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    heads = [(0, 0), (B_ - 1, H // 2), (B_ - 1, H - 1)]
+    rows = sample_rows(Sq, 12, seed=d + H)
+    check_sampled(q, k, v, o, lse, causal, heads, rows, 1.0 / math.sqrt(d), O_TOL["bf16"],
+                  LSE_TOL["bf16"], f"bf16 {B_}x{H}x{Sq}x{Skv} d={d}", bf16_out=False)
+
+
 # ------------------------------------------------------------------ smaller bf16 shapes, whole output
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
