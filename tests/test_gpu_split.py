@@ -12,7 +12,8 @@ import math
 import pytest
 import torch
 
-from parity import O_TOL, LSE_TOL, check_full, gpu_run, log, oracle_full, compare
+from parity import (LSE_TOL, O_TOL, check_full, check_sampled, compare, gpu_run, log,
+                    oracle_full)
 from seeded_inputs import WORKLOADS, make_tensors, random_tensors
 from tiled_online_softmax_05_amd import binding
 
@@ -54,6 +55,22 @@ def test_split_bf16_normal_inputs_fp32_out():
     for causal in (False, True):
         check_full(q, k, v, causal, splits=0, out_dtype=torch.float32,
                    what=f"bf16 N(0,1) split 8x5000 causal={causal}")
+
+
+def test_split_decode_full_size_sampled():
+    """Decode after a long key cache at the long-context head count: B=1,
+    H=64, Sq=16 against Skv=32768, d=128, bf16 N(0,1), end-aligned causal,
+    with the library's chunk count; every query row of three heads against
+    the oracle."""
+    q, k, v = random_tensors(1, 64, 16, 32768, 128, "bf16", "normal", seed=4242)
+    n, chunk = binding.select_splits(128, 16, 32768, 64, binding.BF16, True)
+    log(f"split decode 16x32768 H=64: {n} chunks of {chunk} keys")
+    assert n > 1
+    o, lse = gpu_run(q, k, v, True, splits=0, out_dtype=torch.float32)
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    check_sampled(q, k, v, o, lse, True, [(0, 0), (0, 31), (0, 63)], range(16),
+                  1.0 / math.sqrt(128), O_TOL["bf16"], LSE_TOL["bf16"],
+                  "split decode 16x32768", bf16_out=False)
 
 
 def test_split_rows_without_keys():
