@@ -211,3 +211,13 @@ def _split(lib, n_splits=2, ws=0x600000, ws_bytes=1 << 20, **kw):
 def test_split_invalid_arguments_rejected_on_host(lib, kw, status):
     assert _split(lib, **kw) == status
     assert lib.attn_last_error().decode() != ""
+
+
+def test_sequence_length_limit_per_head(lib):
+    # one head's Q, K or V is addressed with 32-bit byte offsets: S * d * 4 must
+    # stay below 2^31 (4-byte elements assumed for every dtype)
+    smax = (2 ** 31 - 1) // (128 * 4)                  # 4194303 rows at d = 128
+    for dtype in (B.F32, B.BF16):
+        assert _call(lib, Skv=smax + 1, d=128, dtype=dtype) == B.ERR_INVALID_ARG
+        assert "too long" in lib.attn_last_error().decode()
+        assert _call(lib, Sq=smax + 1, d=128, dtype=dtype) == B.ERR_INVALID_ARG
