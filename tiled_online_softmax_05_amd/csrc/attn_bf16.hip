@@ -22,21 +22,12 @@
 // of the next contraction O^T = V^T P^T.
 //
 // Exponentials are base 2 with scale * log2(e) folded into one FMA; the
-// running reference m is kept in that scaled base-2 domain.  The online
-// normalisation gives the same O and LSE (up to rounding) for any choice of
-// reference point as long as the exponentials stay in range, and the kernel
-// uses that freedom: the first key tile of a query tile takes its row
-// maxima and sets m from them (lazily, see kSlack, when m is already set);
-// every later tile reuses m with no maximum, rescale or branch, and each
-// lane records the largest sum of one tile's probabilities it produced.
-// The query tile's results are written only if no lane's per-tile sum
-// exceeded kLaneSumMax (every probability then stayed at or below 2^16).
-// Otherwise the workgroup runs the tile again with m preset: a first sweep
-// over its key tiles takes every row's maximum over all of them, and the
-// same pipeline then runs from those maxima, every probability at most 1.
-// A row that sees any key of its range sees the range's first key
-// (visibility is a prefix of the keys), so the first tile gives every such
-// row a finite m.
+// running maximum m is kept in that scaled base-2 domain.  Every key tile
+// takes its row maxima (in-lane, then one exchange with lane c + 32) and
+// updates m as the online normalisation prescribes, lazily: m moves, and l
+// and the accumulator are rescaled by 2^(m_old - m_new), only when a tile's
+// maximum exceeds m by more than kSlack.  Probabilities therefore never
+// exceed 2^kSlack, and most tiles skip the rescale.
 #include "attn.h"
 #include "attn_internal.h"
 #include "attn_device.h"
@@ -48,18 +39,12 @@ namespace attn {
 namespace {
 
 constexpr float kLog2ef = 1.44269504088896341f;
-// Slack of the running reference, in base-2 exponent units: the reference
-// point m moves (and l and a are rescaled by 2^(m_old - m_new)) only when a
-// tile's maximum exceeds it by more than this, so probabilities stay below
-// 2^kSlack = 256 and most tiles skip the accumulator rescale.
+// Slack of the running maximum, in base-2 exponent units: m moves (and l
+// and a are rescaled by 2^(m_old - m_new)) only when a tile's maximum
+// exceeds it by more than this, so every probability stays at or below
+// 2^kSlack = 256 (well inside fp16's range as well as bf16's) and most
+// tiles skip the accumulator rescale.
 constexpr float kSlack = 8.f;
-// Bound on a lane's sum of one tile's probabilities (its 16 values of one
-// row against the reference of the first tile), which bounds every
-// probability by 2^16: far from overflow in the fp32 sums and accumulators
-// and in the 16-bit P operand, whose relative precision does not depend on
-// magnitude.  Scores that exceed the first tile's maximum by more than 16
-// (base 2) send the query tile to the pass with its maxima preset.
-constexpr float kLaneSumMax = 65536.f;
 constexpr float kLn2f = 0.693147180559945309f;
 
 // Key held by LDS row r (0..31) of a 32-key block: D row 8a + 4h + b of the
@@ -218,7 +203,6 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     __shared__ __attribute__((aligned(16))) T sV1[BN * D];
     __shared__ __attribute__((aligned(16))) T sV2[BN * D];
     __shared__ __attribute__((aligned(16))) T sV3[BN * D];
-    __shared__ int s_vote[WAVES];      // per-wave vote of the fast pass
     // vmcnt value that leaves exactly one step's DMA (K and V) in flight
     constexpr int kWaitOlderDma = wait_vmcnt(2 * PER);
     static_assert(5 * PER < 64, "DMA counts must fit the 6-bit vmcnt field");
@@ -291,10 +275,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     }
 
     // ---- one query tile: Q operand, online softmax over its key tiles, O/LSE ----
-    // preset: take the rows' maxima over all key tiles first and start from
-    // them (no vote); otherwise the first tile's maxima, then the vote.
-    // Returns false, having written nothing, when the vote fails.
-    auto run_tile = [&](int qt, bool preset) __attribute__((always_inline)) -> bool {
+    auto run_tile = [&](int qt) __attribute__((always_inline)) {
     const int q0w = qt * BM + wave * 32;
     const int qi = q0w + c;
 
@@ -316,10 +297,9 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
-    float m = -INFINITY;     // running reference, scale*log2(e) units
+    float m = -INFINITY;     // running maximum, scale*log2(e) units
     float m_ref = 0.f;       // m, or 0 while the row has seen no key
     float l = 0.f;           // this lane's part of the normaliser
-    float pmax = 0.f;        // fast pass: largest per-tile sum of this lane
     f32x16 acc[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
@@ -379,29 +359,26 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     };
 
     // One step of the skewed pipeline.  While the VALU turns the scores st
-    // of tile j into probabilities pn (and, when EX, moves m and l), the
-    // matrix cores compute the scores sn of tile j + 1 from K in sk (when QK)
-    // and add P_{j-1} V_{j-1} (probabilities po, V in sv) to the accumulator
-    // (when PV).  Score and P.V MFMAs alternate, so each has softmax work to
-    // hide under it.  EX (the first tile) takes the row maximum first and
-    // moves the accumulator to a new reference only after the P.V MFMAs,
-    // and only when some row of the wave raised it; the other tiles take
-    // their exponentials against the current reference from the first slot.
-    // The first two K and V operands arrive in kp / vp, read during the
-    // previous step; with PF the step reads those of the next step from
-    // sk_pre / sv_pre in their place.
-    auto fused = [&](auto QK, auto PV, auto EX, auto PF, const T* __restrict__ sk,
+    // of tile j into probabilities pn and moves m and l, the matrix cores
+    // compute the scores sn of tile j + 1 from K in sk (when QK) and add
+    // P_{j-1} V_{j-1} (probabilities po, V in sv) to the accumulator (when
+    // PV).  Score and P.V MFMAs alternate, so each has softmax work to hide
+    // under it.  The row maximum of tile j comes first (slots 0 and 1); the
+    // accumulator moves to a new m only after the P.V MFMAs, and only when
+    // some row of the wave raised it.  The first two K and V operands arrive
+    // in kp / vp, read during the previous step; with PF the step reads
+    // those of the next step from sk_pre / sv_pre in their place.
+    auto fused = [&](auto QK, auto PV, auto PF, const T* __restrict__ sk,
                      const T* __restrict__ sv, const f32x16* st, f32x16* sn,
                      const V8 (*po)[2], V8 (*pn)[2], V8* kp, V8* vp,
                      const T* __restrict__ sk_pre,
                      const T* __restrict__ sv_pre) __attribute__((always_inline)) {
         constexpr bool qk = decltype(QK)::value;
         constexpr bool pv = decltype(PV)::value;
-        constexpr bool ex_max = decltype(EX)::value;
         constexpr bool pf = decltype(PF)::value;
         constexpr int NM = (qk ? NA : 0) + (pv ? NB : 0);   // MFMAs of the step
         constexpr int NS = NM > 4 ? NM : 4;                  // schedule slots
-        constexpr int S0 = ex_max ? 2 : 0;                   // first slot with exponentials
+        constexpr int S0 = 2;                                // first slot with exponentials
         V8 ka[3], va[3];
         if constexpr (qk) {
             ka[0] = kp[0];
@@ -457,25 +434,23 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 acc[i] = mfma_32x32x16(va[t % 3], po[u / 2][u % 2],
                                                                  acc[i], 0, 0, 0);
             }
-            if constexpr (ex_max) {
-                if (s == 0) {
+            if (s == 0) {
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-                }
-                if (s == 1) {
-                    mx = other_half_max(mx);
-                    const float mt = mx * sl2;              // tile max, scaled base-2 domain
-                    const bool grow = mt > m + kSlack;      // true on the first visible tile
-                    // 2^(m - mt): 0 when m = -inf; no rescale (1) while m stays put
-                    alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
-                    m = grow ? mt : m;
-                    m_ref = (m == -INFINITY) ? 0.f : m;     // 0 while the row has seen no key
-                    rescale = __any(grow);
-                    pin(alpha);
-                    pin(m_ref);
-                }
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+            }
+            if (s == 1) {
+                mx = other_half_max(mx);
+                const float mt = mx * sl2;              // tile max, scaled base-2 domain
+                const bool grow = mt > m + kSlack;      // true on the row's first visible tile
+                // 2^(m - mt): 0 when m = -inf; no rescale (1) while m stays put
+                alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+                m = grow ? mt : m;
+                m_ref = (m == -INFINITY) ? 0.f : m;     // 0 while the row has seen no key
+                rescale = __any(grow);
+                pin(alpha);
+                pin(m_ref);
             }
             if (s >= S0) {
                 // exponentials of values [e0, e1) of this slot; the row sum
@@ -498,19 +473,12 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             vp[1] = v_operand(sv_pre, 1);
         }
         sum_pack((NS - S0 - 1) * NV / (NS - S0), NV);     // the last slot's values
-        if constexpr (ex_max) {
-            l = l * alpha + psum;
-            // acc holds sum_{t <= j-1} relative to the old reference; move it
-            // to the new one before P_j V_j is added in the next step
-            if (rescale) {
+        l = l * alpha + psum;
+        // acc holds sum_{t <= j-1} relative to the old maximum; move it to
+        // the new one before P_j V_j is added in the next step
+        if (rescale) {
 #pragma unroll
-                for (int i = 0; i < ND; ++i) acc[i] *= alpha;
-            }
-        } else {
-            l += psum;
-            // (a NaN sum is not counted here; it reaches l and propagates
-            // as it would in the exact pass)
-            pmax = fmaxf(pmax, psum);
+            for (int i = 0; i < ND; ++i) acc[i] *= alpha;
         }
     };
 
@@ -541,7 +509,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // scoped no-alias metadata, which lets the compiler see that the DMA into
     // the free buffers never overlaps the operand reads of the busy ones (the
     // transposing read otherwise waits for all DMA in flight).
-    auto step = [&](auto PV, auto EX, int j, f32x16* st, V8 (*po)[2], V8* kp, V8* vp,
+    auto step = [&](auto PV, int j, f32x16* st, V8 (*po)[2], V8* kp, V8* vp,
                     const T* __restrict__ k_next, const T* __restrict__ k_pre,
                     T* __restrict__ k_free, const T* __restrict__ v_prev,
                     const T* __restrict__ v_pre, T* __restrict__ v_free) {
@@ -551,7 +519,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         mask(kv0, st);
         f32x16 sn[NKB];
         V8 pn[NKB][2];
-        fused(T_{}, PV, EX, T_{}, k_next, v_prev, st, sn, po, pn, kp, vp, k_pre, v_pre);
+        fused(T_{}, PV, T_{}, k_next, v_prev, st, sn, po, pn, kp, vp, k_pre, v_pre);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             st[kb] = sn[kb];
@@ -561,36 +529,6 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         __builtin_amdgcn_s_waitcnt(kWaitOlderDma);   // K_{j+3}, V_{j+1} have landed
         ring_barrier();
     };
-
-    if (preset) {
-        // Row maxima over all visible key tiles, scores computed exactly as
-        // in the pipeline (same operands, same order), so no tile of the
-        // pass that follows exceeds them and every probability is at most 1.
-        float mx = -INFINITY;
-        for (int t = 0; t < n_tiles; ++t) {
-            const int kv0 = kv_begin + t * BN;
-            load_k(kv0, sK0);
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __syncthreads();
-            f32x16 sc[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                sc[kb] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    sc[kb] = mfma_32x32x16(k_operand(sK0, ks * NKB + kb), qop[ks], sc[kb],
-                                           0, 0, 0);
-            }
-            mask(kv0, sc);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-            __syncthreads();      // every wave has read sK0 before the next tile
-        }
-        m = other_half_max(mx) * sl2;
-        m_ref = (m == -INFINITY) ? 0.f : m;
-    }
 
     if (n_tiles > 0) {
         // ---- prologue: K_0 .. K_3, V_0, V_1 in flight; S_0 from K_0 ----
@@ -625,25 +563,25 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         kp[1] = k_operand(sK1, 1);
         int j = 0;
         if (n_tiles > 1) {
-            // no P.V yet; the row maximum sets the reference of either pass
-            step(F_{}, T_{}, 0, st, po, kp, vp, sK1, sK2, sK0, sV3, sV0, sV2);
+            // no P.V yet
+            step(F_{}, 0, st, po, kp, vp, sK1, sK2, sK0, sV3, sV0, sV2);
             j = 1;
             for (; j + 4 < n_tiles; j += 4) {
-                step(T_{}, F_{}, j, st, po, kp, vp, sK2, sK3, sK1, sV0, sV1, sV3);
-                step(T_{}, F_{}, j + 1, st, po, kp, vp, sK3, sK0, sK2, sV1, sV2, sV0);
-                step(T_{}, F_{}, j + 2, st, po, kp, vp, sK0, sK1, sK3, sV2, sV3, sV1);
-                step(T_{}, F_{}, j + 3, st, po, kp, vp, sK1, sK2, sK0, sV3, sV0, sV2);
+                step(T_{}, j, st, po, kp, vp, sK2, sK3, sK1, sV0, sV1, sV3);
+                step(T_{}, j + 1, st, po, kp, vp, sK3, sK0, sK2, sV1, sV2, sV0);
+                step(T_{}, j + 2, st, po, kp, vp, sK0, sK1, sK3, sV2, sV3, sV1);
+                step(T_{}, j + 3, st, po, kp, vp, sK1, sK2, sK0, sV3, sV0, sV2);
             }
             if (j + 1 < n_tiles) {               // j % 4 == 1 here
-                step(T_{}, F_{}, j, st, po, kp, vp, sK2, sK3, sK1, sV0, sV1, sV3);
+                step(T_{}, j, st, po, kp, vp, sK2, sK3, sK1, sV0, sV1, sV3);
                 ++j;
             }
             if (j + 1 < n_tiles) {
-                step(T_{}, F_{}, j, st, po, kp, vp, sK3, sK0, sK2, sV1, sV2, sV0);
+                step(T_{}, j, st, po, kp, vp, sK3, sK0, sK2, sV1, sV2, sV0);
                 ++j;
             }
             if (j + 1 < n_tiles) {
-                step(T_{}, F_{}, j, st, po, kp, vp, sK0, sK1, sK3, sV2, sV3, sV1);
+                step(T_{}, j, st, po, kp, vp, sK0, sK1, sK3, sV2, sV3, sV1);
                 ++j;
             }
         }
@@ -658,28 +596,12 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
         mask(kv_begin + j * BN, st);
         V8 pn[NKB][2];
         if (j > 0)
-            fused(F_{}, T_{}, F_{}, F_{}, nullptr, v_prev, st, nullptr, po, pn, kp, vp, nullptr,
+            fused(F_{}, T_{}, F_{}, nullptr, v_prev, st, nullptr, po, pn, kp, vp, nullptr,
                   nullptr);
         else
-            fused(F_{}, F_{}, T_{}, F_{}, nullptr, nullptr, st, nullptr, po, pn, kp, vp, nullptr,
+            fused(F_{}, F_{}, F_{}, nullptr, nullptr, st, nullptr, po, pn, kp, vp, nullptr,
                   nullptr);
         pv_tile(v_last, pn);
-    }
-
-    if (!preset) {
-        // Workgroup vote: every wave's rows stayed within kLaneSumMax, or
-        // the whole workgroup runs this query tile again with its maxima
-        // preset (the K/V ring is shared, so the decision must be common).
-        // Each wave writes its own slot; the barrier that precedes the next
-        // use of the slots (the next query tile or the preset pass) keeps a
-        // wave from overwriting a slot another wave still reads.
-        const bool within = __all(pmax <= kLaneSumMax);
-        if (lane == 0) s_vote[wave] = within ? 1 : 0;
-        __syncthreads();
-        int votes = 0;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) votes += s_vote[w];
-        if (votes != WAVES) return false;
     }
 
     // ---- epilogue: O = a / l, LSE = ln 2 * (m + log2 l) ----
@@ -723,25 +645,15 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                 LSE[row] = lt > 0.f ? (m + log2f(lt)) * kLn2f : -INFINITY;
         }
     }
-    return true;
     };
 
-    // The query tiles of the workgroup in turn, each again with its maxima
-    // preset when its vote fails; one copy of the pipeline serves every pass
-    // (each pass after the first starts with a barrier: the LDS buffers and
-    // vote slots are reused).
-    int qt = qt_first;
-    bool preset = false;
-#pragma nounroll
-    while (true) {
-        if (run_tile(qt, preset)) {
-            if (qt == qt_second || qt_second < 0) break;
-            qt = qt_second;
-            preset = false;
-        } else {
-            preset = true;
-        }
+    // The query tiles of the workgroup in turn; one copy of the pipeline
+    // serves both (the second starts after a barrier: the LDS buffers are
+    // reused).
+    run_tile(qt_first);
+    if (qt_second >= 0) {
         __syncthreads();
+        run_tile(qt_second);
     }
 }
 
