@@ -168,77 +168,79 @@ def direct_attention_rows(q_head, row_ids: Sequence[int], k_head, v_head, Sq: in
 
 
 def online_tiled_attention(q, k, v, block_q: int, block_kv: int, scale: float | None = None,
-                           causal: bool = False, rescale_previous_acc: bool = True
+                           causal: bool = False, rescale_accumulator: bool = True
                            ) -> Tuple[np.ndarray, np.ndarray, Dict[str, int]]:
     """The tiled online-softmax method on one head, in float64 -- used only to
     check the oracle against the pages' own tiled results, never as the
     reference for the GPU.
 
-    Follows "Online normalization" on "Tiled attention: preserving results
-    without a full score matrix" and the tiled lab function of "Verify tiled
-    attention" ("Keep the softmax state between tiles"): queries are split
-    into tiles of ``block_q`` rows; each row keeps a running maximum ``m``
-    (initially -inf), a denominator ``l`` and an unnormalised accumulator
-    ``a`` (initially 0).  Key/value tiles of ``block_kv`` rows are visited in
-    order; for causal attention the visit stops at the first key tile that no
-    row of the query tile can see.  For each visited tile and each row with at
-    least one visible key in it:
+    The recurrence of "Online normalization" on "Tiled attention: preserving
+    results without a full score matrix" (also "Keep the softmax state
+    between tiles" on "Verify tiled attention"), written per query tile with
+    whole-tile array operations.  Every row of a query tile of ``block_q``
+    rows carries a running maximum ``mx`` (initially -inf), a normaliser
+    ``den`` and an unnormalised output ``num`` (initially 0).  The key tiles
+    of ``block_kv`` rows are taken in order -- for causal attention up to the
+    last one any row of the query tile can see -- and each one updates the
+    state of every row through its visibility mask:
 
-        m_new   = max(m, max_j S_j)
-        rescale = exp(m - m_new)            (0 while m is still -inf)
-        P_j     = exp(S_j - m_new)
-        a       = a * rescale + sum_j P_j v_j
-        l       = l * rescale + sum_j P_j
-        m       = m_new
+        tile_max = max over the row's visible keys of the tile's scores
+        new_max  = max(mx, tile_max)
+        shrink   = exp(mx - new_max)              (0 while mx is -inf)
+        w        = exp(scores - new_max) on visible keys, 0 elsewhere
+        num      = shrink * num + w @ v_tile
+        den      = shrink * den + sum(w)
+        mx       = new_max
 
-    and finally ``O = a / l``.  ``rescale_previous_acc=False`` reproduces the
-    mistake the pages warn about: ``l`` is rescaled but ``a`` is not.
+    Rows with no visible key in a tile keep their state.  At the end
+    ``O = num / den`` and ``LSE = mx + ln den``; rows that never saw a key
+    give O = 0 and LSE = -inf.  ``rescale_accumulator=False`` is the mistake
+    the pages warn about: ``den`` shrinks with the maximum but ``num`` does
+    not.
 
-    ``q`` is ``[Sq, d]``, ``k`` and ``v`` ``[Skv, d]``.  Returns ``(O, LSE,
-    meta)`` with ``meta["tiles_visited"]`` the number of (query tile, key
-    tile) pairs visited and ``meta["max_score_tile_elements"] = block_q *
-    block_kv``."""
+    ``q`` is ``[Sq, d]``, ``k`` and ``v`` ``[Skv, d]``; the causal mask is
+    aligned to the end of the keys.  Returns ``(O, LSE, counters)`` with
+    ``counters["tiles_visited"]`` the number of (query tile, key tile) pairs
+    visited and ``counters["max_score_tile_elements"] = block_q * block_kv``."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     Sq, d = q.shape
     Skv = k.shape[0]
+    dv = v.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if block_q <= 0 or block_kv <= 0:
         raise ValueError("tile sizes must be positive")
-    out = np.zeros((Sq, v.shape[1]), dtype=np.float64)
+    # one past the last visible key of every query row
+    seen = np.array([last_visible_key(i, Sq, Skv, causal) for i in range(Sq)], dtype=np.int64)
+    out = np.zeros((Sq, dv), dtype=np.float64)
     lse = np.full((Sq,), NEG_INF, dtype=np.float64)
-    tiles_visited = 0
-    offset = Skv - Sq
-    for q0 in range(0, Sq, block_q):
-        q1 = min(q0 + block_q, Sq)
-        m = [NEG_INF] * (q1 - q0)
-        l = [0.0] * (q1 - q0)
-        a = np.zeros((q1 - q0, v.shape[1]), dtype=np.float64)
-        for k0 in range(0, Skv, block_kv):
-            # causal: the tile's last row sees keys up to (q1 - 1) + offset
-            if causal and k0 > (q1 - 1) + offset:
-                break
-            k1 = min(k0 + block_kv, Skv)
-            tiles_visited += 1
-            for r in range(q1 - q0):
-                i = q0 + r
-                n = last_visible_key(i, Sq, Skv, causal)
-                cols = range(k0, min(k1, n))
-                if len(cols) == 0:
-                    continue
-                S = (k[k0:k0 + len(cols)] @ q[i]) * scale
-                m_new = max(m[r], float(S.max()))
-                rescale = math.exp(m[r] - m_new) if m[r] > NEG_INF else 0.0
-                P = np.exp(S - m_new)
-                acc_scale = rescale if rescale_previous_acc else 1.0
-                a[r] = a[r] * acc_scale + P @ v[k0:k0 + len(cols)]
-                l[r] = l[r] * rescale + float(P.sum())
-                m[r] = m_new
-        for r in range(q1 - q0):
-            if l[r] > 0.0:
-                out[q0 + r] = a[r] / l[r]
-                lse[q0 + r] = m[r] + math.log(l[r])
-    return out, lse, {"tiles_visited": tiles_visited,
+    pairs = 0
+    for lo in range(0, Sq, block_q):
+        hi = min(lo + block_q, Sq)
+        rows = slice(lo, hi)
+        mx = np.full(hi - lo, NEG_INF)
+        den = np.zeros(hi - lo)
+        num = np.zeros((hi - lo, dv))
+        key_end = int(seen[rows].max()) if causal else Skv
+        for kl in range(0, key_end, block_kv):
+            kh = min(kl + block_kv, Skv)
+            pairs += 1
+            visible = np.arange(kl, kh)[None, :] < seen[rows, None]          # [rows, keys]
+            scores = (q[rows] @ k[kl:kh].T) * scale
+            live = visible.any(axis=1)                                       # rows that see a key here
+            tile_max = np.where(visible, scores, NEG_INF).max(axis=1)
+            new_max = np.where(live, np.maximum(mx, tile_max), mx)
+            with np.errstate(invalid="ignore"):
+                shrink = np.where(mx > NEG_INF, np.exp(mx - new_max), 0.0)
+            shrink = np.where(live, shrink, 1.0)
+            w = np.where(visible, np.exp(scores - np.where(live, new_max, 0.0)[:, None]), 0.0)
+            num = (shrink[:, None] if rescale_accumulator else 1.0) * num + w @ v[kl:kh]
+            den = shrink * den + w.sum(axis=1)
+            mx = new_max
+        has = den > 0.0
+        out[lo:hi][has] = num[has] / den[has, None]
+        lse[lo:hi][has] = mx[has] + np.log(den[has])
+    return out, lse, {"tiles_visited": pairs,
                       "max_score_tile_elements": block_q * block_kv,
                       "materialized_nxn_elements": 0}
 

@@ -101,7 +101,7 @@ def test_omitting_accumulator_rescale_is_caught():
     o, _ = oracle.direct_attention(q, k, v, causal=True)
     good, _, _ = oracle.online_tiled_attention(q, k, v, *c["tiles"], causal=True)
     bad, _, _ = oracle.online_tiled_attention(q, k, v, *c["tiles"], causal=True,
-                                              rescale_previous_acc=False)
+                                              rescale_accumulator=False)
     assert oracle.max_abs_diff(o, good) < c["correct_below"]
     assert oracle.max_abs_diff(o, bad) > c["buggy_above"]
 
