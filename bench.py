@@ -42,6 +42,9 @@ METRIC = "attention fwd TFLOP/s and % MFMA peak (bf16 H=32 S=4096 d=128 causal)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "f64": 78.6}
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_h32_s4096_d128.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_busy_prefill_h32_s4096_d128.json")
+# MI355X: 256 compute units of 4 SIMDs each, in 8 XCDs
+N_SIMDS, N_XCDS = 1024, 8
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_device.h", "attn_api.hip"]
 
 
@@ -77,6 +80,100 @@ def measured_traffic(workload: str):
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+# The counter runs behind the two records (run from the repository root; DIR
+# is the folder passed to --record-counters).
+COUNTER_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_fetch -o run -- "
+    "python3 -u bench.py --steps 20 --warmup 100 --cpu-budget 0",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_write -o run -- "
+    "python3 -u bench.py --steps 20 --warmup 100 --cpu-budget 0",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_copy_fetch -o run -- "
+    "python3 -u bench.py --copy-probe 1073741824 --steps 3",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_copy_write -o run -- "
+    "python3 -u bench.py --copy-probe 1073741824 --steps 3",
+    "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+    "-d DIR/pmc_mfma -o run -- python3 -u bench.py --steps 20 --warmup 100 --cpu-budget 0",
+]
+
+
+def measured_mfma_busy(workload: str):
+    """Fraction of the launch's cycles in which a SIMD's matrix core is busy,
+    from rocprofv3 counters taken on the current kernel source (else None):
+    SQ_VALU_MFMA_BUSY_CYCLES per SIMD over GRBM_GUI_ACTIVE per XCD."""
+    if workload != "prefill_h32_s4096_d128" or not os.path.exists(MFMA_FILE):
+        return None
+    with open(MFMA_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("mfma_busy_frac")
+
+
+def read_counters(path: str, kernel_key: str = "attn_fwd_bf16_kernel", last: int = 20):
+    """Mean per dispatch of each counter in a rocprofv3 counter_collection.csv,
+    over the last ``last`` dispatches of the kernel whose name contains
+    ``kernel_key`` (the timed launches come last).  Returns (kernel name,
+    {counter: mean})."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if kernel_key not in r["Kernel_Name"]:
+                continue
+            rows.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], {}))[1][r["Counter_Name"]] = \
+                float(r["Counter_Value"])
+    if not rows:
+        raise SystemExit(f"{path}: no dispatch of a kernel named *{kernel_key}*")
+    ids = sorted(rows)[-last:]
+    name = rows[ids[-1]][0]
+    means = {}
+    for c in rows[ids[-1]][1]:
+        means[c] = sum(rows[i][1][c] for i in ids) / len(ids)
+    return name, means
+
+
+def record_counters(d: str, commands: list) -> None:
+    """Write the traffic and MFMA-busy records from the rocprofv3 counter runs
+    under ``d`` (pmc_fetch, pmc_write, pmc_copy_fetch, pmc_copy_write,
+    pmc_mfma, each with a run_counter_collection.csv), keyed on the current
+    kernel source."""
+    def csv_in(sub):
+        return os.path.join(d, sub, "run_counter_collection.csv")
+    name, fetch = read_counters(csv_in("pmc_fetch"))
+    _, write = read_counters(csv_in("pmc_write"))
+    _, cfetch = read_counters(csv_in("pmc_copy_fetch"), kernel_key="", last=1)
+    _, cwrite = read_counters(csv_in("pmc_copy_write"), kernel_key="", last=1)
+    _, mf = read_counters(csv_in("pmc_mfma"))
+    # the copy reads and writes copy_bytes once each: bytes per counted byte
+    copy_bytes = 1 << 30
+    fscale = copy_bytes / (cfetch["FETCH_SIZE"] * 1024)
+    wscale = copy_bytes / (cwrite["WRITE_SIZE"] * 1024)
+    h = kernel_source_hash()
+    rd = round(fetch["FETCH_SIZE"] * 1024 * fscale)
+    wr = round(write["WRITE_SIZE"] * 1024 * wscale)
+    traffic = {"workload": "prefill_h32_s4096_d128", "kernel": name, "kernel_source_sha256_16": h,
+               "fetch_size_kib_per_launch": round(fetch["FETCH_SIZE"], 1),
+               "write_size_kib_per_launch": round(write["WRITE_SIZE"], 1),
+               "copy_probe_bytes": copy_bytes,
+               "copy_fetch_size_kib": round(cfetch["FETCH_SIZE"], 4),
+               "copy_write_size_kib": round(cwrite["WRITE_SIZE"], 4),
+               "fetch_scale": round(fscale, 5), "write_scale": round(wscale, 5),
+               "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+               "hbm_bytes_per_launch": rd + wr, "commands": commands[:4]}
+    busy = mf["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMDS
+    active = mf["GRBM_GUI_ACTIVE"] / N_XCDS
+    mfma = {"workload": "prefill_h32_s4096_d128", "kernel": name, "kernel_source_sha256_16": h,
+            "sq_valu_mfma_busy_cycles": mf["SQ_VALU_MFMA_BUSY_CYCLES"],
+            "grbm_gui_active": mf["GRBM_GUI_ACTIVE"], "simds": N_SIMDS, "xcds": N_XCDS,
+            "mfma_busy_cycles_per_simd": round(busy, 1), "active_cycles_per_xcd": round(active, 1),
+            "mfma_busy_frac": round(busy / active, 4), "commands": commands[4:]}
+    for path, rec in ((TRAFFIC_FILE, traffic), (MFMA_FILE, mfma)):
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(f"wrote {path}")
 
 
 def cpu_baseline(q, k, v, causal: bool, budget_s: float) -> dict:
@@ -195,8 +292,14 @@ def main(argv=None) -> int:
                     help="overwrite a 1 GiB buffer before each timed launch (outside the "
                          "per-launch events), so K/V start outside L2 and Infinity Cache; "
                          "value then comes from the events")
+    ap.add_argument("--record-counters", metavar="DIR", default=None,
+                    help="no GPU: write the traffic and MFMA-busy records from the rocprofv3 "
+                         "counter runs under DIR (see profiles/) for the current kernel source")
     a = ap.parse_args(argv)
 
+    if a.record_counters:
+        record_counters(a.record_counters, COUNTER_COMMANDS)
+        return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -322,11 +425,13 @@ def main(argv=None) -> int:
     # counters were taken on the default launch (selector tiles, one key chunk, warm cache)
     default_launch = tiles == w.tiles and n_splits is None and not a.flush
     traffic = measured_traffic(a.workload) if default_launch else None
+    mfma_busy = measured_mfma_busy(a.workload) if default_launch else None
 
     # bound: MFMA above the ridge point (peak FLOP/s over HBM bytes/s), HBM below
     if flops / comp >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic}
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                    "mfma_busy_frac": mfma_busy}
     else:
         gbs = comp / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,

@@ -40,3 +40,39 @@ def test_kernel_source_hash_follows_code_not_comments():
     changed[first] = files[first] + "\nstatic int added_symbol;\n"
     assert bench.kernel_source_hash(lambda p: changed[p]) != h0
 
+
+
+def test_counter_records_are_read_back(tmp_path, monkeypatch):
+    """--record-counters turns rocprofv3 counter CSVs into the two records;
+    bench.py reports them while the kernel source hash matches and null
+    otherwise."""
+    import csv as _csv
+    header = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+              "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+              "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+              "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+    def write(sub, kernel, counters, n):
+        d = tmp_path / sub
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = _csv.writer(f)
+            w.writerow(header)
+            for i in range(1, n + 1):
+                for name, value in counters.items():
+                    w.writerow([i, i, "Agent 1", 1, 1, 1, 1, 1, kernel, 256, 0, 0, 0, 0, 0,
+                                name, value, 0, 1])
+    kern = "x_attn_fwd_bf16_kernel_y"
+    write("pmc_fetch", kern, {"FETCH_SIZE": 1000.0}, 25)
+    write("pmc_write", kern, {"WRITE_SIZE": 500.0}, 25)
+    write("pmc_copy_fetch", "copy_kernel", {"FETCH_SIZE": 524288.0}, 3)
+    write("pmc_copy_write", "copy_kernel", {"WRITE_SIZE": 1048576.0}, 3)
+    write("pmc_mfma", kern, {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 600.0, "GRBM_GUI_ACTIVE": 8 * 1000.0}, 25)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    monkeypatch.setattr(bench, "MFMA_FILE", str(tmp_path / "mfma.json"))
+    bench.record_counters(str(tmp_path), bench.COUNTER_COMMANDS)
+    assert bench.measured_traffic("prefill_h32_s4096_d128") == 2 * 1000 * 1024 + 500 * 1024
+    assert bench.measured_mfma_busy("prefill_h32_s4096_d128") == 0.6
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda read=None: "0000000000000000")
+    assert bench.measured_traffic("prefill_h32_s4096_d128") is None
+    assert bench.measured_mfma_busy("prefill_h32_s4096_d128") is None
