@@ -82,8 +82,8 @@ typedef enum {
  *   lse      : output [B, H, Sq] float32, or NULL to skip it.
  *   B, H     : batch and heads (>= 0).
  *   Sq, Skv  : query and key lengths (>= 0).  Sq == 0 is a no-op.
- *   d        : head dimension: 16, 32, 64 or 128 (fp32); 64 or 128 (bf16,
- *              fp16).
+ *   d        : head dimension: 16, 32, 64 or 128 (fp32); 32, 64 or 128
+ *              (bf16, fp16).
  *   scale    : score scale, finite and > 0 (usually 1/sqrt(d)).
  *   causal   : 0 (none), 1 (end-aligned mask above) or 2 (start-aligned).
  *   dtype    : an attn_dtype.
@@ -104,8 +104,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   ATTN_F32            block_m in {16, 32, 64},  block_n in {16, 32, 64}
  *                       (every d)
  *   ATTN_BF16[_OUT_F32], ATTN_F16[_OUT_F32]
- *                       block_m in {64, 128},     block_n in {32, 64},
- *                       and block_m = 256 with block_n = 32 when d = 128
+ *                       block_m in {64, 128},     block_n in {32, 64} (d = 64,
+ *                       128) or block_n = 64 (d = 32), and block_m = 256
+ *                       with block_n = 32 when d = 128
  * Any other pair returns ATTN_ERR_UNSUPPORTED.
  */
 int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -114,7 +115,14 @@ int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * attn_select_tiles -- the tile / occupancy selector (host only, no HIP
- * call).  Writes the tile shape attn_fwd would use for this problem:
+ * call).  "Verify tiled attention", section "Separate storage savings from
+ * runtime": the tile size, register pressure, cache reuse and precision of
+ * the chosen kernel decide its speed, so the choice is made here per head
+ * dimension, dtype and grid size rather than fixed.  On the 16-bit path,
+ * d = 32 takes 64-key tiles (a 32-key tile would give each step only two
+ * score MFMAs, too few to hide the softmax under), d = 64 and 128 take
+ * 32-key tiles.
+ * Writes the tile shape attn_fwd would use for this problem:
  * query rows per workgroup, key rows per tile, 64-wide waves per workgroup
  * and LDS bytes per workgroup.  fp32 waves own 16 query rows each; with
  * 16-row query tiles on a grid of fewer than 512 (1024) query tiles, four

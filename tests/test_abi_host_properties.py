@@ -14,8 +14,8 @@ from tiled_online_softmax_05_amd import binding as B
 # distinct, 16-byte aligned fake device addresses far apart (never dereferenced:
 # every call below fails validation on the host)
 BASE = {"q": 1 << 40, "k": 2 << 40, "v": 3 << 40, "o": 4 << 40, "lse": 5 << 40}
-DIMS = {B.F32: [16, 32, 64, 128], B.BF16: [64, 128], B.BF16_OUT_F32: [64, 128],
-        B.F16: [64, 128], B.F16_OUT_F32: [64, 128]}
+DIMS = {B.F32: [16, 32, 64, 128], B.BF16: [32, 64, 128], B.BF16_OUT_F32: [32, 64, 128],
+        B.F16: [32, 64, 128], B.F16_OUT_F32: [32, 64, 128]}
 FAULTS = ["q_null", "o_null", "k_null", "v_null", "negative_size", "d_nonpositive",
           "d_unsupported", "dtype_unknown", "scale_bad", "causal_bad", "ptr_misaligned",
           "lse_misaligned", "o_overlaps", "tiles_bad"]
@@ -45,7 +45,7 @@ def faulty_call(draw):
             a["d"] = -draw(st.integers(0, 64))
         elif f == "d_unsupported":
             a["d"] = draw(st.sampled_from([8, 24, 48, 96, 256] +
-                                          ([16, 32] if a["dtype"] != B.F32 else [])))
+                                          ([16] if a["dtype"] != B.F32 else [])))
         elif f == "dtype_unknown":
             a["dtype"] = draw(st.sampled_from([-1, 5, 6, 100]))
         elif f == "scale_bad":

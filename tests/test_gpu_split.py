@@ -37,7 +37,7 @@ def test_split_stress_fp32(name, causal):
         check_full(q, k, v, causal, splits=splits, what=f"{name} causal={causal} splits={splits}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Sq,Skv", [(1, 4000), (16, 777), (100, 3000), (300, 333)])
 def test_split_bf16(Sq, Skv, causal, d):

@@ -149,8 +149,8 @@ int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
         t->lds_bytes = f32_lds_bytes(d, bm, bn);
         return ATTN_OK;
     }
-    if (!(d == 64 || d == 128))
-        return fail(ATTN_ERR_UNSUPPORTED, "16-bit head dim %d not built (64, 128)", d);
+    if (!(d == 32 || d == 64 || d == 128))
+        return fail(ATTN_ERR_UNSUPPORTED, "16-bit head dim %d not built (32, 64, 128)", d);
     // Workgroups of 128 query rows (four waves, two workgroups per CU) when
     // that gives every CU a workgroup, else 64; causal workgroups take a heavy
     // and a light query tile each.  32-key tiles: the pipelined kernel holds
@@ -162,7 +162,10 @@ int select(int d, int Sq, int Skv, int BH, int dtype, bool causal, Tiles* t) {
         return (long)BH * (causal ? (n_qt + 1) / 2 : n_qt);
     };
     int bm = items(128) >= kCUs ? 128 : 64;
-    int bn = 32;
+    // d = 32: a 32-key tile would hold only two score MFMAs per step, too few
+    // to hide the softmax under; 64-key tiles (two score tiles of 32 registers
+    // each still fit at two waves per SIMD when d is this small)
+    int bn = d == 32 ? 64 : 32;
     t->block_m = bm;
     t->block_n = bn;
     t->waves = bm / 32;
@@ -211,7 +214,7 @@ int validate(const Problem& p) {
                     p.Sq, p.Skv);
     if (p.d <= 0) return fail(ATTN_ERR_INVALID_ARG, "head dim %d must be positive", p.d);
     if (p.dtype == ATTN_F32 ? !(p.d == 16 || p.d == 32 || p.d == 64 || p.d == 128)
-                            : !(p.d == 64 || p.d == 128))
+                            : !(p.d == 32 || p.d == 64 || p.d == 128))
         return fail(ATTN_ERR_UNSUPPORTED, "head dim %d not built for dtype %d", p.d, p.dtype);
     if (!std::isfinite(p.scale) || !(p.scale > 0.f))
         return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)",

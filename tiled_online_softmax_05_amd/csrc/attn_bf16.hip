@@ -188,7 +188,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     constexpr int NV = 16 * NKB;       // scores per lane per tile
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert(CHUNKS % NT == 0, "every lane moves the same number of chunks");
-    static_assert(DCH == 8 || DCH == 16, "K swizzle covers 8 or 16 chunks per row");
+    static_assert(DCH == 4 || DCH == 8 || DCH == 16, "K swizzle covers 4, 8 or 16 chunks per row");
     static_assert(NA >= 4 && NB >= ND + 1, "schedule needs a few MFMAs per phase");
 
     // Four buffers each for K and V: K_t lives in sK[t % 4], V_t in
@@ -210,12 +210,18 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // K layout in LDS: unpadded rows of DCH 16-byte chunks; chunk q of row r
     // sits at position q ^ k_swz(r).  An operand read (16 lanes = 16
     // consecutive rows, one chunk) then touches 16 distinct 16-byte bank
-    // groups of the 64-bank LDS.
-    auto k_swz = [](int r) { return DCH == 16 ? (r & 15) : ((r >> 1) & 7); };
+    // groups of the 64-bank LDS (with 4 chunks per row, rows r and r + 4
+    // share banks before the swizzle, and (r / 4) % 4 separates them).
+    auto k_swz = [](int r) {
+        return DCH == 16 ? (r & 15) : (DCH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3));
+    };
     // V layout in LDS: row = key, chunk q of row key at q ^ v_swz(key).  The
     // transposing operand read of 32 lanes covers 4 keys x 4 chunks; the
-    // swizzle puts those 16 chunks in 16 distinct bank groups.
-    auto v_swz = [](int key) { return DCH == 16 ? 4 * (key & 3) : 4 * ((key >> 1) & 1); };
+    // swizzle puts those 16 chunks in 16 distinct bank groups (64-byte rows,
+    // d = 32, already do: 4 consecutive keys fill the 256 bytes of the banks).
+    auto v_swz = [](int key) {
+        return DCH == 16 ? 4 * (key & 3) : (DCH == 8 ? 4 * ((key >> 1) & 1) : 0);
+    };
 
     // Workgroup -> (head, query tiles).  Causal: one workgroup runs query
     // tile n_qt-1-r and then tile r, so every workgroup visits the same
@@ -681,20 +687,27 @@ hipError_t launch_one(const Problem& p) {
 
 template <typename T, int D, bool OUT_F32>
 hipError_t by_tiles(const Problem& p, int bm, int bn) {
-    if constexpr (D == 128) {
-        if (bm == 256 && bn == 32) return launch_one<T, D, 32, 8, OUT_F32>(p);
+    if constexpr (D == 32) {
+        // a 32-key tile holds only two score MFMAs at d = 32: 64-key tiles
+        if (bm == 128 && bn == 64) return launch_one<T, D, 64, 4, OUT_F32>(p);
+        if (bm == 64 && bn == 64) return launch_one<T, D, 64, 2, OUT_F32>(p);
+    } else {
+        if constexpr (D == 128) {
+            if (bm == 256 && bn == 32) return launch_one<T, D, 32, 8, OUT_F32>(p);
+        }
+        if (bm == 128 && bn == 64) return launch_one<T, D, 64, 4, OUT_F32>(p);
+        if (bm == 128 && bn == 32) return launch_one<T, D, 32, 4, OUT_F32>(p);
+        if (bm == 64 && bn == 64) return launch_one<T, D, 64, 2, OUT_F32>(p);
+        if (bm == 64 && bn == 32) return launch_one<T, D, 32, 2, OUT_F32>(p);
     }
-    if (bm == 128 && bn == 64) return launch_one<T, D, 64, 4, OUT_F32>(p);
-    if (bm == 128 && bn == 32) return launch_one<T, D, 32, 4, OUT_F32>(p);
-    if (bm == 64 && bn == 64) return launch_one<T, D, 64, 2, OUT_F32>(p);
-    if (bm == 64 && bn == 32) return launch_one<T, D, 32, 2, OUT_F32>(p);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool bf16_tiles_supported(int d, int block_m, int block_n) {
-    if (!(d == 64 || d == 128)) return false;
+    if (!(d == 32 || d == 64 || d == 128)) return false;
+    if (d == 32) return (block_m == 64 || block_m == 128) && block_n == 64;
     if (block_m == 256) return d == 128 && block_n == 32;
     return (block_m == 64 || block_m == 128) && (block_n == 32 || block_n == 64);
 }
@@ -709,6 +722,9 @@ hipError_t by_dim(const Problem& p, const Tiles& t, bool out_f32) {
     if (p.d == 128)
         return out_f32 ? by_tiles<T, 128, true>(p, t.block_m, t.block_n)
                        : by_tiles<T, 128, false>(p, t.block_m, t.block_n);
+    if (p.d == 32)
+        return out_f32 ? by_tiles<T, 32, true>(p, t.block_m, t.block_n)
+                       : by_tiles<T, 32, false>(p, t.block_m, t.block_n);
     return out_f32 ? by_tiles<T, 64, true>(p, t.block_m, t.block_n)
                    : by_tiles<T, 64, false>(p, t.block_m, t.block_n);
 }
