@@ -187,6 +187,34 @@ int attn_select_splits(int d, int Sq, int Skv, int BH, int dtype, int causal,
  */
 long long attn_split_workspace_bytes(int B, int H, int Sq, int d, int n_splits);
 
+/*
+ * attn_fwd_split_noalloc -- attn_fwd_split for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  It allocates nothing (no hipMalloc, hipFree or
+ * allocating library call); the key chunks' partial states go to a static
+ * device array of ATTN_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * copy per device, held from the library's first use on that device until
+ * the process ends.  Its address is looked up once per device, on the
+ * first call made with that device current.
+ *
+ *   q ... n_splits : as attn_fwd_split; the call runs on the current
+ *                    device, and `stream` (if not NULL) must belong to it.
+ * The chunk plan, kernels and results are those of attn_fwd_split with the
+ * same arguments (bitwise).  The scratch needs no clearing: every byte a
+ * call reads was written earlier in the same call.  All calls on one device
+ * share its array: calls that overlap in time on one device (different
+ * streams, host threads) race and give wrong results; calls in one stream
+ * are ordered and safe.
+ * Returns as attn_fwd_split; ATTN_ERR_INVALID_ARG (nothing enqueued) when
+ * the chunks that would run need more than ATTN_NOALLOC_SCRATCH_BYTES
+ * (attn_split_workspace_bytes of that chunk count) or `stream` belongs to
+ * another device; ATTN_ERR_HIP if the array's address cannot be found.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Sq, int Skv, int d, float scale, int causal,
+                           int dtype, void* stream, int n_splits);
+
 /* attn_last_error -- message for the last non-OK status on this thread
  * ("" if none).  The string stays valid until the next call on the thread. */
 const char* attn_last_error(void);

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert lib.attn_version() == 101
+    assert lib.attn_version() == 102
 
 
 @pytest.mark.parametrize("args,want", [
@@ -224,3 +224,42 @@ def test_sequence_length_limit_per_head(lib):
         assert _call(lib, Skv=smax + 1, d=128, dtype=dtype) == B.ERR_INVALID_ARG
         assert "too long" in lib.attn_last_error().decode()
         assert _call(lib, Sq=smax + 1, d=128, dtype=dtype) == B.ERR_INVALID_ARG
+
+
+def _noalloc(lib, n_splits, Sq, H=64, Skv=4096, d=128, dtype=B.BF16, causal=0):
+    # addresses 4 GiB apart: never dereferenced, and far enough apart that
+    # no overlap check fires first
+    g = 1 << 32
+    return lib.attn_fwd_split_noalloc(g, 2 * g, 3 * g, 4 * g, 5 * g, 1, H, Sq, Skv, d, 0.125,
+                                      causal, dtype, None, n_splits)
+
+
+def test_noalloc_rejects_more_than_its_scratch(lib):
+    # 64 heads x 256 query rows x 16 chunks of 256 keys at d = 128 need
+    # 16 * 16384 * (512 + 8) bytes, beyond the static scratch: refused on the
+    # host, with the sizes in the message, before any HIP call
+    need = B.split_workspace_bytes(1, 64, 256, 128, 16)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, 16, 256) == B.ERR_INVALID_ARG
+    msg = lib.attn_last_error().decode()
+    assert "scratch" in msg and str(need) in msg and str(B.NOALLOC_SCRATCH_BYTES) in msg
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_splits=-1), B.ERR_INVALID_ARG),
+    (dict(n_splits=5000), B.ERR_INVALID_ARG),
+    (dict(causal=3), B.ERR_INVALID_ARG),
+    (dict(d=48), B.ERR_UNSUPPORTED),
+    (dict(dtype=9), B.ERR_INVALID_ARG),
+])
+def test_noalloc_invalid_arguments_rejected_on_host(lib, kw, status):
+    args = dict(n_splits=2, Sq=8)
+    args.update(kw)
+    assert _noalloc(lib, **args) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES

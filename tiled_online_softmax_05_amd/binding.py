@@ -30,8 +30,10 @@ STATUS_NAMES = {OK: "ATTN_OK", ERR_INVALID_ARG: "ATTN_ERR_INVALID_ARG",
                 ERR_HIP: "ATTN_ERR_HIP"}
 
 EXPORTED = ("attn_fwd", "attn_fwd_tiles", "attn_select_tiles", "attn_fwd_split",
-            "attn_select_splits", "attn_split_workspace_bytes", "attn_last_error",
-            "attn_version")
+            "attn_select_splits", "attn_split_workspace_bytes", "attn_fwd_split_noalloc",
+            "attn_last_error", "attn_version")
+# bytes of the library's static per-device scratch (attn_fwd_split_noalloc)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class AttnError(RuntimeError):
@@ -66,6 +68,8 @@ def load() -> ctypes.CDLL:
         ll = ctypes.c_longlong
         lib.attn_fwd_split.argtypes = fwd_args + [ip, vp, ll]
         lib.attn_fwd_split.restype = ip
+        lib.attn_fwd_split_noalloc.argtypes = fwd_args + [ip]
+        lib.attn_fwd_split_noalloc.restype = ip
         lib.attn_select_splits.argtypes = [ip, ip, ip, ip, ip, ip, pi, pi]
         lib.attn_select_splits.restype = ip
         lib.attn_split_workspace_bytes.argtypes = [ip, ip, ip, ip, ip]
@@ -158,11 +162,22 @@ def fwd_split_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: Optio
                                 ws_ptr, int(ws_bytes)))
 
 
+def fwd_split_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int,
+                          lse_ptr: Optional[int], B: int, H: int, Sq: int, Skv: int, d: int,
+                          scale: float, causal: bool, dtype: int, stream: int,
+                          n_splits: int) -> None:
+    """Direct call of ``attn_fwd_split_noalloc`` on raw device pointers (the
+    library's static scratch holds the chunks' partial states)."""
+    check(load().attn_fwd_split_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Sq, Skv, d,
+                                        float(scale), int(causal), dtype, stream,
+                                        int(n_splits)))
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
         tiles: Optional[Tuple[int, int]] = None, with_lse: bool = True,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-        splits: Optional[int] = None
+        splits: Optional[int] = None, noalloc: bool = False
         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """O, LSE = attention(q, k, v) on the GPU through ``attn_fwd``.
 
@@ -171,8 +186,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     ``1/sqrt(d)``.  ``tiles=(block_m, block_n)`` forces a tile shape.
     ``causal`` is False/True (end-aligned) or ``CAUSAL_START``.
     ``splits`` (an int, 0 = the library's choice) calls ``attn_fwd_split``
-    instead, with a workspace allocated here.  The call is enqueued on torch's
-    current stream of q's device."""
+    instead, with a workspace allocated here, or -- with ``noalloc=True`` --
+    ``attn_fwd_split_noalloc``, which uses the library's static scratch (pass
+    ``out`` and ``lse`` as well for a call that allocates nothing).  The call
+    is enqueued on torch's current stream of q's device."""
     lib = load()
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors (there is no CPU path)")
@@ -199,6 +216,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale = 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     lse_ptr = lse.data_ptr() if lse is not None else None
+    if noalloc and splits is None:
+        raise ValueError("noalloc applies to the split path: give splits as well")
     with torch.cuda.device(q.device):
         if splits is None:
             fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr, B, H, Sq,
@@ -206,6 +225,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         else:
             if tiles is not None:
                 raise ValueError("tiles and splits cannot be combined")
+            if noalloc:
+                fwd_split_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse_ptr, B, H, Sq, Skv, d, scale, causal, code, stream,
+                                      int(splits))
+                return out, lse
             n = int(splits) if splits > 0 else select_splits(d, Sq, Skv, B * H, code, causal)[0]
             nbytes = split_workspace_bytes(B, H, Sq, d, max(n, 1))
             ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)

@@ -5,11 +5,18 @@
 #include "attn_device.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
+
+// Partial states of attn_fwd_split_noalloc's key chunks.  Each device keeps
+// its own copy at its own address; host code uses that address, never this
+// name, which on the host is only a stand-in for the symbol.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace attn {
 namespace {
@@ -247,10 +254,51 @@ int validate(const Problem& p) {
     return ATTN_OK;
 }
 
+// Device address of `scratch` per device, found once per device with that
+// device current.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_on_current_device(hipStream_t stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ATTN_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch covers",
+                    dev, kMaxDevices);
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess)
+            return fail(ATTN_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(ATTN_ERR_INVALID_ARG, "stream belongs to device %d, device %d is current",
+                        (int)sdev, dev);
+    }
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || ptr == nullptr)
+                return fail(ATTN_ERR_HIP, "no address for the static scratch on device %d: %s",
+                            dev, hipGetErrorString(e));
+            if ((reinterpret_cast<uintptr_t>(ptr) & 255u) != 0)
+                return fail(ATTN_ERR_HIP, "static scratch on device %d is not 256-byte aligned",
+                            dev);
+            g_scratch[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return ATTN_OK;
+}
+
 // want_splits < 0: no split (attn_fwd); >= 0: attn_fwd_split with the
-// caller's workspace.
+// caller's workspace, or with the static scratch when `static_scratch`.
 int run(const Problem& p_in, int block_m, int block_n, int want_splits = -1,
-        void* workspace = nullptr, int64_t workspace_bytes = 0) {
+        void* workspace = nullptr, int64_t workspace_bytes = 0, bool static_scratch = false) {
     Problem p = p_in;
     int st = validate(p);
     if (st != ATTN_OK) return st;
@@ -301,6 +349,17 @@ int run(const Problem& p_in, int block_m, int block_n, int want_splits = -1,
         if (n > 1) {
             const int64_t rows = (int64_t)bh * p.Sq;
             const int64_t need = split_workspace(rows, p.d, n);
+            if (static_scratch) {
+                if (need > ATTN_NOALLOC_SCRATCH_BYTES)
+                    return fail(ATTN_ERR_INVALID_ARG,
+                                "%d key chunks over %lld query rows need %lld bytes of scratch, "
+                                "more than the static %lld",
+                                n, (long long)rows, (long long)need,
+                                (long long)ATTN_NOALLOC_SCRATCH_BYTES);
+                st = scratch_on_current_device(p.stream, &workspace);
+                if (st != ATTN_OK) return st;
+                workspace_bytes = ATTN_NOALLOC_SCRATCH_BYTES;
+            }
             if (workspace == nullptr || workspace_bytes < need)
                 return fail(ATTN_ERR_INVALID_ARG, "workspace of %lld bytes too small (need %lld)",
                             (long long)workspace_bytes, (long long)need);
@@ -383,6 +442,20 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
     return attn::run(p, 0, 0, n_splits, workspace, workspace_bytes);
 }
 
+int attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Sq, int Skv, int d, float scale, int causal,
+                           int dtype, void* stream, int n_splits) {
+    if (causal < 0 || causal > 2)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "causal must be 0, 1 or 2 (got %d)", causal);
+    if (n_splits < 0 || n_splits > 4096)
+        return attn::fail(ATTN_ERR_INVALID_ARG, "n_splits must be in [0, 4096] (got %d)",
+                          n_splits);
+    attn::Problem p{q, k, v, o, lse, B, H, Sq, Skv, d, scale, causal != 0, dtype,
+                    static_cast<hipStream_t>(stream)};
+    p.causal_off = causal == 2 ? 0 : Skv - Sq;
+    return attn::run(p, 0, 0, n_splits, nullptr, 0, true);
+}
+
 int attn_select_splits(int d, int Sq, int Skv, int BH, int dtype, int causal, int* n_splits,
                        int* kv_chunk) {
     int bm = 0, bn = 0, waves = 0, lds = 0;
@@ -407,6 +480,6 @@ long long attn_split_workspace_bytes(int B, int H, int Sq, int d, int n_splits) 
 
 const char* attn_last_error(void) { return attn::g_last_error.c_str(); }
 
-int attn_version(void) { return 101; }
+int attn_version(void) { return 102; }
 
 }  // extern "C"
