@@ -653,13 +653,15 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     }
     };
 
-    // The query tiles of the workgroup in turn; one copy of the pipeline
-    // serves both (the second starts after a barrier: the LDS buffers are
+    // The query tiles of the workgroup in turn, through one copy of the
+    // pipeline (the second starts after a barrier: the LDS buffers are
     // reused).
-    run_tile(qt_first);
-    if (qt_second >= 0) {
-        __syncthreads();
-        run_tile(qt_second);
+#pragma nounroll
+    for (int t = 0; t < 2; ++t) {
+        const int qt = t == 0 ? qt_first : qt_second;
+        if (qt < 0) break;
+        if (t > 0) __syncthreads();
+        run_tile(qt);
     }
 }
 
