@@ -23,11 +23,16 @@
 //
 // Exponentials are base 2 with scale * log2(e) folded into one FMA; the
 // running maximum m is kept in that scaled base-2 domain.  Every key tile
-// takes its row maxima (in-lane, then one exchange with lane c + 32) and
-// updates m as the online normalisation prescribes, lazily: m moves, and l
-// and the accumulator are rescaled by 2^(m_old - m_new), only when a tile's
-// maximum exceeds m by more than kSlack.  Probabilities therefore never
-// exceed 2^kSlack, and most tiles skip the rescale.
+// takes its row maxima and updates m as the online normalisation
+// prescribes, lazily: m moves, and l and the accumulator are rescaled by
+// 2^(m_old - m_new), only when a tile's maximum exceeds m by more than
+// kSlack.  The test runs on raw scores against thr = (m + kSlack) /
+// (scale log2 e), on each lane's half of its row (a row passes exactly when
+// one half does), so the common tile costs one compare per lane; the
+// exchange with lane c + 32 and the rescale run in a wave-uniform branch
+// only on tiles where some row passes.  Probabilities therefore stay at
+// 2^kSlack or below (up to the rounding of thr), and most tiles skip the
+// rescale.
 #include "attn.h"
 #include "attn_internal.h"
 #include "attn_device.h"
@@ -41,9 +46,9 @@ namespace {
 constexpr float kLog2ef = 1.44269504088896341f;
 // Slack of the running maximum, in base-2 exponent units: m moves (and l
 // and a are rescaled by 2^(m_old - m_new)) only when a tile's maximum
-// exceeds it by more than this, so every probability stays at or below
-// 2^kSlack = 256 (well inside fp16's range as well as bf16's) and most
-// tiles skip the accumulator rescale.
+// exceeds it by more than this, so every probability stays at about
+// 2^kSlack = 256 or below (well inside fp16's range as well as bf16's) and
+// most tiles skip the accumulator rescale.
 constexpr float kSlack = 8.f;
 constexpr float kLn2f = 0.693147180559945309f;
 
@@ -128,10 +133,15 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 __device__ __forceinline__ float other_half_max(float x) {
-    // v_permlane32_swap: lane l (< 32) receives lane l + 32 and vice versa
+    // v_permlane32_swap: lane l (< 32) receives lane l + 32 and vice versa.
+    // The maximum as one plain v_max_f32: fmaxf would first quiet both
+    // values (two more instructions), which scores that are finite or -inf
+    // never need.
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                     false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return m;
 }
 
 __device__ __forceinline__ float other_half_sum(float x) {
@@ -305,6 +315,8 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
 
     float m = -INFINITY;     // running maximum, scale*log2(e) units
     float m_ref = 0.f;       // m, or 0 while the row has seen no key
+    float thr = -INFINITY;   // (m + kSlack) / (scale log2 e): a raw tile maximum
+                             // above it moves m
     float l = 0.f;           // this lane's part of the normaliser
     f32x16 acc[ND];
 #pragma unroll
@@ -369,7 +381,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     // compute the scores sn of tile j + 1 from K in sk (when QK) and add
     // P_{j-1} V_{j-1} (probabilities po, V in sv) to the accumulator (when
     // PV).  Score and P.V MFMAs alternate, so each has softmax work to hide
-    // under it.  The row maximum of tile j comes first (slots 0 and 1); the
+    // under it.  The row-maximum test of tile j comes first (slots 0 and 1); the
     // accumulator moves to a new m only after the P.V MFMAs, and only when
     // some row of the wave raised it.  The first two K and V operands arrive
     // in kp / vp, read during the previous step; with PF the step reads
@@ -396,7 +408,10 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             va[0] = vp[0];
             va[1] = vp[1];
         }
-        float mx = -INFINITY, alpha = 1.f, psum = 0.f;
+        // (psum starts at -0, which an added value replaces exactly, so no
+        // add of the start value is issued; alpha is set and read only when
+        // the step rescales)
+        float mx = -INFINITY, alpha, psum = -0.f;
         bool rescale = false;
         // While it interleaves MFMAs and softmax, the wave outranks a wave of
         // the other workgroup on the same SIMD that is issuing DMA, waiting at
@@ -447,16 +462,25 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
             }
             if (s == 1) {
-                mx = other_half_max(mx);
-                const float mt = mx * sl2;              // tile max, scaled base-2 domain
-                const bool grow = mt > m + kSlack;      // true on the row's first visible tile
-                // 2^(m - mt): 0 when m = -inf; no rescale (1) while m stays put
-                alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
-                m = grow ? mt : m;
-                m_ref = (m == -INFINITY) ? 0.f : m;     // 0 while the row has seen no key
-                rescale = __any(grow);
-                pin(alpha);
-                pin(m_ref);
+                // mx covers this lane's half of the row's values: a row's
+                // maximum passes its threshold exactly when one half does
+                rescale = __any(mx > thr);
+                // (rare: the maximum moves on few tiles; a wave-uniform branch)
+                if (rescale) {
+                    mx = other_half_max(mx);            // the row's maximum
+                    const bool grow = mx > thr;         // true on the row's first visible tile
+                    const float mt = mx * sl2;          // tile max, scaled base-2 domain
+                    // 2^(m - mt): 0 when m = -inf; no rescale (1) while m stays put
+                    alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+                    m = grow ? mt : m;
+                    m_ref = (m == -INFINITY) ? 0.f : m;     // 0 while the row has seen no key
+                    thr = (m + kSlack) / sl2;
+                    pin(thr);
+                    // (volatile: keeps the compiler from turning the branch
+                    // into selects that compute all of this on every tile)
+                    pin(alpha);
+                    pin(m_ref);
+                }
             }
             if (s >= S0) {
                 // exponentials of values [e0, e1) of this slot; the row sum
@@ -479,13 +503,14 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
             vp[1] = v_operand(sv_pre, 1);
         }
         sum_pack((NS - S0 - 1) * NV / (NS - S0), NV);     // the last slot's values
-        l = l * alpha + psum;
         // acc holds sum_{t <= j-1} relative to the old maximum; move it to
         // the new one before P_j V_j is added in the next step
         if (rescale) {
+            l *= alpha;
 #pragma unroll
             for (int i = 0; i < ND; ++i) acc[i] *= alpha;
         }
+        l += psum;
     };
 
     using std::integral_constant;
