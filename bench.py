@@ -267,6 +267,50 @@ def gemm_probe(n: int, steps: int) -> None:
     print(json.dumps(res), flush=True)
 
 
+def mfma_probe(iters: int, grid: int = 512) -> None:
+    """Sustained bf16 matrix-core rate from libattn_probe.so (see
+    include/attn_probe.h): MFMA streams with zero or random operands, with and
+    without 1 KiB of LDS operand reads per MFMA, two 256-thread workgroups per
+    compute unit.  Three untimed launches, then five timed back to back
+    between one HIP event pair on torch's current stream."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "tiled_online_softmax_05_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m tiled_online_softmax_05_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, ip = ctypes.c_void_p, ctypes.c_int
+    lib.attn_probe_mfma.argtypes = [ip, ip, ip, vp, vp]
+    lib.attn_probe_mfma.restype = ip
+    lib.attn_probe_mfma_flops.argtypes = [ip, ip, ip]
+    lib.attn_probe_mfma_flops.restype = ctypes.c_double
+    dev = torch.device("cuda", 0)
+    out = torch.zeros(grid, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = ["mfma_zero", "mfma_random", "mfma_lds_zero", "mfma_lds_random"]
+    res = {"mfma_probe_iters": iters, "grid": grid, "dtype": "bf16"}
+    for kind, name in enumerate(names):
+        def launch():
+            st = lib.attn_probe_mfma(kind, iters, grid, out.data_ptr(), stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"attn_probe_mfma({kind}) returned {st}")
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            launch()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        tf = lib.attn_probe_mfma_flops(kind, iters, grid) / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    print(json.dumps(res), flush=True)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +332,9 @@ def main(argv=None) -> int:
                          "no operand bit toggling); not the benchmark")
     ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
                     help="time an N x N x N bf16 torch.matmul on random and on zero operands")
+    ap.add_argument("--mfma-probe", type=int, default=0, metavar="ITERS",
+                    help="time bare bf16 MFMA streams (zero / random operands, with and "
+                         "without LDS operand reads) from libattn_probe.so")
     ap.add_argument("--flush", action="store_true",
                     help="overwrite a 1 GiB buffer before each timed launch (outside the "
                          "per-launch events), so K/V start outside L2 and Infinity Cache; "
@@ -314,6 +361,9 @@ def main(argv=None) -> int:
         return 0
     if a.gemm_probe:
         gemm_probe(a.gemm_probe, max(1, a.steps))
+        return 0
+    if a.mfma_probe:
+        mfma_probe(a.mfma_probe)
         return 0
 
     from seeded_inputs import WORKLOADS, make_tensors

@@ -263,3 +263,29 @@ def test_noalloc_scratch_size_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "attn_probe.h")
+
+
+def test_probe_library_exports_its_header_and_rejects_bad_kinds():
+    # the matrix-core rate probe (measurement only): every function the probe
+    # header declares is exported, an invalid kind is refused before any HIP
+    # call, and the FLOP count is 16 MFMAs of 32x32x16 per iteration per wave
+    path = os.path.join(os.path.dirname(B.lib_path()), "libattn_probe.so")
+    assert os.path.exists(path), "libattn_probe.so is not built"
+    probe = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = re.findall(r"^\s*(?:int|double)\s+(attn_probe_\w+)\s*\(", text, flags=re.M)
+    assert sorted(names) == ["attn_probe_mfma", "attn_probe_mfma_flops"]
+    for n in names:
+        getattr(probe, n)
+    probe.attn_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    probe.attn_probe_mfma_flops.argtypes = [ctypes.c_int] * 3
+    probe.attn_probe_mfma_flops.restype = ctypes.c_double
+    assert probe.attn_probe_mfma(-1, 10, 4, 0x1000, None) == 1
+    assert probe.attn_probe_mfma(4, 10, 4, 0x1000, None) == 1
+    assert probe.attn_probe_mfma(0, 0, 4, 0x1000, None) == 1
+    assert probe.attn_probe_mfma(0, 10, 4, None, None) == 1
+    assert probe.attn_probe_mfma_flops(1, 10, 4) == 16 * 2 * 32 * 32 * 16 * 10 * 4 * 4

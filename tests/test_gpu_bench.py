@@ -47,3 +47,13 @@ def test_hbm_bound_workload_reports_bandwidth():
     assert ro["bound"] == "hbm" and ro["unit"] == "GB/s" and ro["peak"] == 8000.0
     assert rec["config"]["key_chunks"] > 1
     assert "cpu_baseline" not in rec
+
+
+def test_mfma_probe_line():
+    # the matrix-core rate probe: constant operands must run at least as fast
+    # as random ones, and nothing may beat the published peak
+    rec = run_bench("--mfma-probe", "400")
+    for name in ("mfma_zero", "mfma_random", "mfma_lds_zero", "mfma_lds_random"):
+        r = rec[name]
+        assert 0 < r["frac_of_peak"] <= 1.0, (name, r)
+    assert rec["mfma_zero"]["tflops"] >= 0.9 * rec["mfma_random"]["tflops"]

@@ -1,4 +1,6 @@
-"""Build libattn.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
+"""Build libattn.so (the gfx950 HIP kernels and the C ABI) and
+libattn_probe.so (a matrix-core rate probe used by ``bench.py --mfma-probe``)
+in-tree with hipcc.
 
     python -m tiled_online_softmax_05_amd.build [--jobs N]
 
@@ -23,6 +25,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.hip", "attn_f32.hip", "attn_bf16.hip"]
+PROBE_SOURCES = ["probe_mfma.hip"]
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
 ARCH = "gfx950"
 
 
@@ -49,21 +53,26 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(jobs: int = 4, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile all sources and link libattn.so next to this file.  Always
-    rebuilds.  Returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra or [])
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 4, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile all sources and link libattn.so and libattn_probe.so next to
+    this file.  Always rebuilds.  Returns the path of libattn.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra or [])
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -243,6 +243,8 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int c = lane & 31;
+    // raw-score units per scaled base-2 unit, for the running-maximum test
+    const float inv_sl2 = 1.f / sl2;
 
     const T* Qh = Q + (size_t)bh * Sq * D;
     const T* Kh = K + (size_t)bh * Skv * D;
@@ -474,7 +476,7 @@ void attn_fwd_bf16_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                     alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
                     m = grow ? mt : m;
                     m_ref = (m == -INFINITY) ? 0.f : m;     // 0 while the row has seen no key
-                    thr = (m + kSlack) / sl2;
+                    thr = (m + kSlack) * inv_sl2;
                     pin(thr);
                     // (volatile: keeps the compiler from turning the branch
                     // into selects that compute all of this on every tile)
