@@ -148,3 +148,19 @@ def test_rise_at_fp16_limit(delta, dtype, tiles):
             assert torch.isfinite(o).all() and not torch.isnan(lse).any()
             check_full(q, k, v, causal, scale=scale, tiles=tiles, out_dtype=torch.float32,
                        what=f"rise {delta} d={d} ->f32")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("scale", [1e-3, 0.02, 1.0, 4.0])
+def test_threshold_across_scales(dtype, scale):
+    # the running-maximum test compares raw scores with (m + 8) / (scale
+    # log2 e): tiny scales make that threshold huge, large ones put many
+    # rises in every row; rising scores (x6 from key 150) at d = 64 and 128
+    for d in (64, 128):
+        q, k, v = rising(1, 2, 96, 300, d, 6.0, 150, seed=81, dtype=dtype)
+        for causal in (False, True):
+            log(f"threshold scale={scale} d={d} {dtype} causal={causal}")
+            o, lse, o_ref, lse_ref = check_full(q, k, v, causal, scale=scale,
+                                                out_dtype=torch.float32,
+                                                what=f"scale {scale} d={d}")
+            assert torch.isfinite(o).all() and torch.isfinite(lse).all()
