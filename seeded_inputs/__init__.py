@@ -22,6 +22,9 @@ reference implementation, in full"):
   the logical-access sweep on "Verify tiled attention").
 * ``longctx_h64_s32768_d128`` -- B = 1, H = 64, S = 32768, d = 128, causal,
   standard normal rounded to bf16.
+* ``prefill_h32_s4096_d128_f16``, ``prefill_h32_s4096_d64``,
+  ``prefill_h32_s4096_d32`` -- the S = 4096 prefill in fp16, and in bf16 at
+  the other 16-bit head dims.
 * ``stress_b3h2_d32_skv{64,257,1000,1024}`` and ``stress_b3h2_d32_sq1000`` --
   B = 3, H = 2, d = 32, fp32; Q and K uniform(-0.8, 0.8) times 20 (scores
   of magnitude ~100 and above, the "increase score magnitudes" exercise of
@@ -84,6 +87,12 @@ WORKLOADS: Dict[str, Workload] = {
         # 2-byte element the byte model of "Verify tiled attention" assumes)
         Workload("prefill_h32_s4096_d128_f16", 1, 32, 4096, 4096, 128, "f16", "uniform0.8",
                  306, (True,)),
+        # the same prefill at the other 16-bit head dims (same FLOP formula,
+        # 4 B H Sq Skv d / 2), for their rates
+        Workload("prefill_h32_s4096_d64", 1, 32, 4096, 4096, 64, "bf16", "uniform0.8",
+                 307, (True,)),
+        Workload("prefill_h32_s4096_d32", 1, 32, 4096, 4096, 32, "bf16", "uniform0.8",
+                 308, (True,)),
         _stress("stress_b3h2_d32_skv64", 8, 64, 501, (False, True)),
         _stress("stress_b3h2_d32_skv257", 8, 257, 502, (False, True)),
         _stress("stress_b3h2_d32_skv1000", 8, 1000, 503, (False, True)),

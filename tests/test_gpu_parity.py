@@ -76,6 +76,18 @@ def test_prefill_h32_s4096_d128_full(prefill):
     compare(o, lse, o_ref, lse_ref, O_TOL["bf16"], LSE_TOL["bf16"], "prefill_h32_s4096_d128")
 
 
+@pytest.mark.parametrize("name", ["prefill_h32_s4096_d64", "prefill_h32_s4096_d32"])
+def test_prefill_other_head_dims_full(name):
+    """The S = 4096 causal prefill at d = 64 and 32 (selector tiles, bf16
+    output), every element against the fp64 oracle."""
+    w = WORKLOADS[name]
+    q, k, v = make_tensors(w)
+    log(f"{name} causal, selector tiles, whole output")
+    o, lse = gpu_run(q, k, v, True)
+    o_ref, lse_ref = oracle_full(q, k, v, True)
+    compare(o, lse, o_ref, lse_ref, O_TOL["bf16"], LSE_TOL["bf16"], name)
+
+
 def test_prefill_determinism(prefill):
     w, q, k, v = prefill
     o1, l1 = gpu_run(q, k, v, True)
