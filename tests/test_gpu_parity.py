@@ -342,3 +342,15 @@ def test_p1_pinned_example_d16_on_gpu():
         pr = g["printed"]
         assert np.max(np.abs(oc[0, :4] - pr["sample_row0_first4"])) <= 5e-7 + 1e-6
         assert np.max(np.abs(oc[63, :4] - pr["sample_last_row_first4"])) <= 5e-7 + 1e-6
+
+
+@pytest.mark.parametrize("Sq,Skv", [(1000, 1000), (1008, 700), (700, 1300)])
+@pytest.mark.parametrize("causal", [True, 2], ids=["end", "start"])
+def test_fp32_paired_causal_tiles(Sq, Skv, causal):
+    # causal fp32 grids with more query tiles than compute units run two
+    # query tiles per workgroup (heavy, then light); odd and even tile
+    # counts, both mask alignments, the split path on top
+    q, k, v = random_tensors(2, 3, Sq, Skv, 64, "f32", "normal", seed=Sq + Skv)
+    log(f"fp32 paired causal={causal} {Sq}x{Skv}")
+    check_full(q, k, v, causal, what=f"fp32 paired {Sq}x{Skv} causal={causal}")
+    check_full(q, k, v, causal, splits=3, what=f"fp32 paired split {Sq}x{Skv} causal={causal}")

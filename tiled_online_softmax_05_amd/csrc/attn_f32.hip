@@ -44,7 +44,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
                          const float* __restrict__ V, float* __restrict__ O,
                          float* __restrict__ LSE, int n_bh, int Sq, int Skv, double scale,
                          int n_qt, int off, int kv_chunk, float* __restrict__ part_o,
-                         double* __restrict__ part_lse) {
+                         double* __restrict__ part_lse, int paired) {
     constexpr int WAVES = WQ * KW;
     constexpr int BM = 16 * WQ;
     constexpr int NT = 64 * WAVES;
@@ -59,8 +59,16 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     __shared__ __attribute__((aligned(16))) float sK[BN * KP];
     __shared__ __attribute__((aligned(16))) float sV[BN * VP];
 
-    int bh, qt;
-    tile_coords(n_bh, n_qt, CAUSAL, bh, qt);
+    // Causal grids with more query tiles than compute units pair them: the
+    // workgroup runs query tile n_qt-1-r and then tile r, so all workgroups
+    // carry about the same number of key tiles.  Smaller grids keep one tile
+    // per workgroup (heaviest first), where running two in a row would only
+    // lengthen the longest path.
+    int bh, qt_first, qt_second = -1;
+    if (CAUSAL && paired)
+        tile_pair_coords(n_bh, n_qt, true, bh, qt_first, qt_second);
+    else
+        tile_coords(n_bh, n_qt, CAUSAL, bh, qt_first);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -68,12 +76,15 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     const int kg = wave / WQ;      // key group of the wave
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int qi = qt * BM + wq * 16 + c;
     const int kw0 = kg * KB;       // first key of a tile this wave takes
 
     const float* Qh = Q + (size_t)bh * Sq * D;
     const float* Kh = K + (size_t)bh * Skv * D;
     const float* Vh = V + (size_t)bh * Skv * D;
+
+    // ---- one query tile ----
+    auto run_tile = [&](int qt) __attribute__((always_inline)) {
+    const int qi = qt * BM + wq * 16 + c;
 
     // Q^T operand, widened to fp64: q[qi][g*DQ + t].
     double qreg[DQ];
@@ -242,7 +253,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
             red_l[kg * 16 + c] = lt;
         }
         __syncthreads();
-        if (kg != 0) return;       // key group 0 finishes the rows
+        if (kg != 0) return;       // key group 0 finishes the rows (of this tile)
         double M = -INFINITY;
 #pragma unroll
         for (int k = 0; k < KW; ++k) M = fmax(M, red_m[k * 16 + c]);
@@ -280,6 +291,17 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
             if (g == 0) part_lse[prow] = lse;
         }
     }
+    };
+
+    // The query tiles of the workgroup in turn, through one copy of the tile
+    // code (the second starts after a barrier: the LDS buffers are reused).
+#pragma nounroll
+    for (int t = 0; t < 2; ++t) {
+        const int qt = t == 0 ? qt_first : qt_second;
+        if (qt < 0) break;
+        if (t > 0) __syncthreads();
+        run_tile(qt);
+    }
 }
 
 template <int D, int BN, int WQ, int KW>
@@ -287,7 +309,10 @@ hipError_t launch_one(const Problem& p) {
     constexpr int BM = 16 * WQ;
     const int n_bh = p.B * p.H;
     const int n_qt = (p.Sq + BM - 1) / BM;
-    const dim3 grid((unsigned)(n_bh * n_qt), (unsigned)p.n_splits);
+    // pair causal query tiles when there are more of them than compute units
+    const int paired = p.causal && (long)n_bh * n_qt > 256 ? 1 : 0;
+    const dim3 grid((unsigned)(n_bh * (paired ? tile_pair_count(n_qt, true) : n_qt)),
+                    (unsigned)p.n_splits);
     const dim3 block(64 * WQ * KW);
     const double scale = (double)p.scale;
     const float* q = static_cast<const float*>(p.q);
@@ -297,11 +322,11 @@ hipError_t launch_one(const Problem& p) {
     if (p.causal)
         hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WQ, KW, true>), grid, block, 0, p.stream,
                            q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.causal_off, p.kv_chunk,
-                           p.part_o, p.part_lse);
+                           p.part_o, p.part_lse, paired);
     else
         hipLaunchKernelGGL((attn_fwd_f32_kernel<D, BN, WQ, KW, false>), grid, block, 0, p.stream,
                            q, k, v, o, p.lse, n_bh, p.Sq, p.Skv, scale, n_qt, p.causal_off, p.kv_chunk,
-                           p.part_o, p.part_lse);
+                           p.part_o, p.part_lse, paired);
     return hipGetLastError();
 }
 
