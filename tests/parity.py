@@ -35,13 +35,14 @@ def kind(t: torch.Tensor) -> str:
 
 
 def gpu_run(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
-            scale: Optional[float] = None, out_dtype=None, tiles=None, splits=None
-            ) -> Tuple[torch.Tensor, torch.Tensor]:
+            scale: Optional[float] = None, out_dtype=None, tiles=None, splits=None,
+            noalloc: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Copy host inputs to cuda:0, run attn_fwd (attn_fwd_split when
-    ``splits`` is an int), return device O and LSE."""
+    ``splits`` is an int, attn_fwd_split_noalloc with ``noalloc``), return
+    device O and LSE."""
     dev = torch.device("cuda", 0)
     o, lse = binding.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale,
-                         out_dtype=out_dtype, tiles=tiles, splits=splits)
+                         out_dtype=out_dtype, tiles=tiles, splits=splits, noalloc=noalloc)
     torch.cuda.synchronize()
     return o, lse
 
@@ -91,9 +92,9 @@ def oracle_full(q, k, v, causal, scale: Optional[float] = None):
 
 
 def check_full(q, k, v, causal: bool, scale=None, out_dtype=None, tiles=None, what="",
-               splits=None):
+               splits=None, noalloc: bool = False):
     """Whole-output parity at the strict tolerance of the input dtype."""
-    o, lse = gpu_run(q, k, v, causal, scale, out_dtype, tiles, splits)
+    o, lse = gpu_run(q, k, v, causal, scale, out_dtype, tiles, splits, noalloc)
     o_ref, lse_ref = oracle_full(q, k, v, causal, scale)
     compare(o, lse, o_ref, lse_ref, O_TOL[kind(q)], LSE_TOL[kind(q)], what)
     return o, lse, o_ref, lse_ref

@@ -1,9 +1,17 @@
-"""Whole-output parity on a seeded sweep of random small problems: batch,
-heads, query and key lengths (empty, single, ragged), head dim, dtype, output
-dtype, mask (none, end- or start-aligned), forced tile shape or the
-selector, and the split path with chosen or automatic chunk counts.  Each
-case is compared element by element with the fp64 oracle at the input
-dtype's tolerance; the list of cases is fixed by one seed."""
+"""Whole-output parity on a seeded sweep of random problems: batch, heads,
+query and key lengths (empty, single, ragged, up to a few thousand), head
+dim, dtype, output dtype, mask (none, end- or start-aligned), input
+distribution (uniform(-0.8, 0.8), N(0, 1), and the x20 score-magnitude
+stress of "Tiled attention: preserving results without a full score
+matrix", section "Recorded results"), forced tile shape or the selector,
+and the split path with chosen or automatic chunk counts, through the
+caller's workspace or the library's static scratch.  Each case is compared
+element by element with the fp64 oracle at the input dtype's tolerance; the
+list of cases is fixed by one seed.
+
+ATTN_RANDOM_CASES and ATTN_RANDOM_SEED widen or move the sweep (defaults:
+400 cases, seed 2024), e.g. ATTN_RANDOM_CASES=5000 for a long run."""
+import os
 import random
 
 import pytest
@@ -11,44 +19,75 @@ import torch
 
 from parity import check_full, log
 from seeded_inputs import random_tensors
+from tiled_online_softmax_05_amd import binding
 
 pytestmark = pytest.mark.gpu
 
-TILES = {"f32": {16: [(16, 16), (32, 64), (64, 32)], 32: [(16, 64), (64, 16)],
-                 64: [(32, 32), (64, 64)], 128: [(16, 32), (64, 64)]},
-         "bf16": {32: [(128, 64), (64, 64)], 64: [(128, 32), (64, 64), (64, 32)],
-                  128: [(256, 32), (128, 64), (64, 32)]}}
+TILES = {"f32": {16: [(16, 16), (32, 64), (64, 32), (16, 64)],
+                 32: [(16, 64), (64, 16), (32, 32)],
+                 64: [(32, 32), (64, 64), (16, 64)], 128: [(16, 32), (64, 64)]},
+         "bf16": {32: [(128, 64), (64, 64)], 64: [(128, 32), (64, 64), (64, 32), (128, 64)],
+                  128: [(256, 32), (128, 64), (64, 32), (128, 32), (64, 64)]}}
 TILES["f16"] = TILES["bf16"]
+CODE = {("f32", False): binding.F32, ("bf16", False): binding.BF16,
+        ("bf16", True): binding.BF16_OUT_F32, ("f16", False): binding.F16,
+        ("f16", True): binding.F16_OUT_F32}
 
 
-def cases(n, seed=2024):
+def cases(n, seed):
     rng = random.Random(seed)
     out = []
     for i in range(n):
-        dt = rng.choice(["f32", "bf16", "f16"])
+        dt = rng.choice(["f32", "bf16", "f16", "bf16"])
         d = rng.choice([16, 32, 64, 128] if dt == "f32" else [32, 64, 128])
-        B, H = rng.choice([1, 2]), rng.choice([1, 2, 3])
-        Sq = rng.choice([1, 2, rng.randint(3, 70), rng.randint(70, 260)])
-        Skv = rng.choice([0, 1, rng.randint(2, 90), rng.randint(90, 400)])
+        B, H = rng.choice([1, 2, 3]), rng.choice([1, 2, 3, 5])
+        Sq = rng.choice([0, 1, 2, rng.randint(3, 130), rng.randint(130, 700),
+                         rng.randint(700, 2100)])
+        Skv = rng.choice([0, 1, rng.randint(2, 200), rng.randint(200, 1500),
+                          rng.randint(1500, 4500)])
         causal = rng.choice([0, 1, 2])
-        mode = rng.choice(["selector", "tiles", "split"])
+        mode = rng.choice(["selector", "tiles", "split", "noalloc"])
         tiles = rng.choice(TILES[dt][d]) if mode == "tiles" else None
-        splits = rng.choice([0, 2, 5]) if mode == "split" else None
-        dist = rng.choice(["uniform0.8", "normal"])
+        splits = rng.choice([0, 2, 3, 7]) if mode in ("split", "noalloc") else None
+        dist = rng.choice(["uniform0.8", "normal", "stress"])
         # N(0, 1) inputs put |O| near 4, where storing O in 16 bits alone
         # costs up to half an ulp (1.6e-2 in bf16): those cases take an fp32 O
-        out_f32 = dt != "f32" and (dist == "normal" or rng.random() < 0.3)
-        out.append((i, dt, d, B, H, Sq, Skv, causal, tiles, splits, out_f32, dist))
+        out_f32 = dt != "f32" and (dist != "uniform0.8" or rng.random() < 0.3)
+        out.append((i, dt, d, B, H, Sq, Skv, causal, tiles, splits, mode == "noalloc",
+                    out_f32, dist))
     return out
 
 
-@pytest.mark.parametrize("case", cases(160), ids=lambda c: f"case{c[0]}")
+N_CASES = int(os.environ.get("ATTN_RANDOM_CASES", "400"))
+SEED = int(os.environ.get("ATTN_RANDOM_SEED", "2024"))
+
+
+@pytest.mark.parametrize("case", cases(N_CASES, SEED), ids=lambda c: f"case{c[0]}")
 def test_random_problem(case):
-    i, dt, d, B, H, Sq, Skv, causal, tiles, splits, out_f32, dist = case
-    what = (f"case {i}: {dt} d={d} B={B} H={H} Sq={Sq} Skv={Skv} causal={causal} "
-            f"tiles={tiles} splits={splits} out_f32={out_f32} {dist}")
+    i, dt, d, B, H, Sq, Skv, causal, tiles, splits, noalloc, out_f32, dist = case
+    what = (f"case {i} (seed {SEED}): {dt} d={d} B={B} H={H} Sq={Sq} Skv={Skv} "
+            f"causal={causal} tiles={tiles} splits={splits} noalloc={noalloc} "
+            f"out_f32={out_f32} {dist}")
     log(what)
-    q, k, v = random_tensors(B, H, Sq, Skv, d, dt, dist, seed=5000 + i)
+    q, k, v = random_tensors(B, H, Sq, Skv, d, dt, dist, seed=5000 + 7919 * SEED + i)
+    if noalloc and B * H * Sq > 0:
+        # the chunk count the call will use is at most this one
+        code = CODE[(dt, out_f32)]
+        n_max = splits or binding.select_splits(d, Sq, Skv, B * H, code, bool(causal))[0]
+        if binding.split_workspace_bytes(B, H, Sq, d, max(n_max, 1)) > \
+                binding.NOALLOC_SCRATCH_BYTES:
+            # may not fit the static scratch: either a clean rejection or a
+            # correct result
+            dev = torch.device("cuda", 0)
+            try:
+                binding.fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal,
+                            out_dtype=torch.float32 if out_f32 else None, splits=splits,
+                            noalloc=True)
+            except binding.AttnError as e:
+                assert e.status == binding.ERR_INVALID_ARG and "scratch" in str(e), str(e)
+                log("  rejected: more scratch than the static buffer holds")
+                return
     o, lse, o_ref, lse_ref = check_full(q, k, v, causal, tiles=tiles, splits=splits,
-                                        out_dtype=torch.float32 if out_f32 else None, what=what)
+                                        out_dtype=torch.float32 if out_f32 else None,
+                                        what=what, noalloc=noalloc)
     assert not torch.isnan(o).any() and not torch.isnan(lse).any()
