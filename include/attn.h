@@ -102,7 +102,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * function on "Verify tiled attention").  block_m = block_n = 0 means "use
  * the selector".  Built shapes:
  *   ATTN_F32            block_m in {16, 32, 64},  block_n in {16, 32, 64}
- *                       (every d)
+ *                       (every d), and block_m = 16 with block_n = 128
  *   ATTN_BF16[_OUT_F32], ATTN_F16[_OUT_F32]
  *                       block_m in {64, 128},     block_n in {32, 64} (d = 64,
  *                       128) or block_n = 64 (d = 32), and block_m = 256
@@ -128,6 +128,9 @@ int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* 
  * 16-row query tiles on a grid of fewer than 512 (1024) query tiles, four
  * (two) waves share each 16-row block, each taking its part of every key
  * tile, and merge their states at the end (at most block_n / 16 waves).
+ * fp32 grids of fewer than 512 such tiles over more than 128 keys at
+ * d <= 64 take 128-key tiles shared by eight waves (16 keys each); forced
+ * 128-key tiles run eight waves, four at d = 128.
  * `BH` is B * H.  Any output pointer may be NULL.  Returns ATTN_OK,
  * ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED.
  */

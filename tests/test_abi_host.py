@@ -45,10 +45,14 @@ def test_version(lib):
     # (d, Sq, Skv, BH, dtype, causal) -> (block_m, block_n, waves)
     # fp32: 16-row query tiles (chosen only while 32-row ones would leave CUs
     # idle, so fewer than 512 of them) with four waves splitting each 64-key
-    # tile; 16-key tiles cannot split
+    # tile, or eight splitting each 128-key tile over more than 128 keys at
+    # d <= 64; 16-key tiles cannot split
     ((32, 64, 64, 1, B.F32, 1), (16, 64, 4)),
-    ((64, 512, 512, 8, B.F32, 0), (16, 64, 4)),
-    ((32, 8, 1000, 6, B.F32, 1), (16, 64, 4)),
+    ((64, 512, 512, 8, B.F32, 0), (16, 128, 8)),
+    ((32, 8, 1000, 6, B.F32, 1), (16, 128, 8)),
+    ((32, 8, 129, 6, B.F32, 1), (16, 128, 8)),
+    ((32, 8, 128, 6, B.F32, 1), (16, 64, 4)),
+    ((128, 8, 1000, 6, B.F32, 0), (16, 64, 4)),        # d = 128 keeps 64-key tiles
     ((32, 8, 16, 6, B.F32, 0), (16, 16, 1)),
     ((64, 2048, 2048, 8, B.F32, 0), (64, 64, 4)),       # four query waves, no key split
     ((128, 4096, 4096, 32, B.BF16, 1), (128, 32, 4)),
@@ -173,10 +177,10 @@ def test_select_splits(lib, args, split):
 
 @pytest.mark.parametrize("args,want", [
     # fp32: four waves per CU (1024 in all; a wave owns 16 query rows)
-    ((64, 512, 512, 8, B.F32, 0), (1, 512)),       # 256 query tiles of four key waves
-    ((32, 1000, 1000, 6, B.F32, 1), (1, 1024)),    # 378 query tiles of four key waves
-    ((32, 8, 1000, 6, B.F32, 0), (16, 64)),        # 24 waves; capped by the 16 key tiles
-    ((32, 16, 4096, 16, B.F32, 0), (16, 256)),     # 16 query tiles x 4 waves -> 16 chunks
+    ((64, 512, 512, 8, B.F32, 0), (1, 512)),       # 256 query tiles of eight key waves
+    ((32, 1000, 1000, 6, B.F32, 1), (1, 1024)),    # 378 query tiles of eight key waves
+    ((32, 8, 1000, 6, B.F32, 0), (8, 128)),        # 48 waves; capped by the 8 key tiles
+    ((32, 16, 4096, 16, B.F32, 0), (8, 512)),      # 16 query tiles x 8 waves -> 8 chunks
     ((64, 2048, 2048, 8, B.F32, 0), (1, 2048)),    # 256 four-wave query tiles already
     # 16-bit: one workgroup per CU (256)
     ((128, 1, 4000, 8, B.BF16, 0), (32, 128)),     # 8 tiles x 32 chunks of 4 key tiles

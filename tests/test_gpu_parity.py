@@ -213,6 +213,8 @@ def test_fp32_ragged_all_tiles(d, causal):
     for bm in (16, 32, 64):
         for bn in (16, 32, 64):
             check_full(q, k, v, causal, tiles=(bm, bn), what=f"fp32 77x133 d={d} ({bm},{bn})")
+    # 128-key tiles (16-row query blocks only): eight key waves, four at d = 128
+    check_full(q, k, v, causal, tiles=(16, 128), what=f"fp32 77x133 d={d} (16,128)")
 
 
 @pytest.mark.parametrize("heads,kw", [(32, 2), (64, 1)], ids=["2 key waves", "1 key wave"])

@@ -23,9 +23,10 @@ from tiled_online_softmax_05_amd import binding
 
 pytestmark = pytest.mark.gpu
 
-TILES = {"f32": {16: [(16, 16), (32, 64), (64, 32), (16, 64)],
-                 32: [(16, 64), (64, 16), (32, 32)],
-                 64: [(32, 32), (64, 64), (16, 64)], 128: [(16, 32), (64, 64)]},
+TILES = {"f32": {16: [(16, 16), (32, 64), (64, 32), (16, 64), (16, 128)],
+                 32: [(16, 64), (64, 16), (32, 32), (16, 128)],
+                 64: [(32, 32), (64, 64), (16, 64), (16, 128)],
+                 128: [(16, 32), (64, 64), (16, 128)]},
          "bf16": {32: [(128, 64), (64, 64)], 64: [(128, 32), (64, 64), (64, 32), (128, 64)],
                   128: [(256, 32), (128, 64), (64, 32), (128, 32), (64, 64)]}}
 TILES["f16"] = TILES["bf16"]

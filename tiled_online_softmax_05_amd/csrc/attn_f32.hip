@@ -123,7 +123,7 @@ void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ 
     // one pass.
     constexpr int NE = BN * (D / 4);
     constexpr int PF = NE % NT == 0 ? NE / NT : 0;
-    constexpr bool kPrefetch = PF > 0 && PF <= 8;
+    constexpr bool kPrefetch = PF > 0 && PF <= (KW == 8 ? 4 : 8);
     f32x4 kpf[kPrefetch ? PF : 1], vpf[kPrefetch ? PF : 1];
     auto fetch_vec = [&](int kv0, int e, f32x4& kx, f32x4& vx) {
         const int row = e / (D / 4);
@@ -333,11 +333,17 @@ hipError_t launch_one(const Problem& p) {
 template <int D, int BN>
 hipError_t by_waves(const Problem& p, int wq, int kw) {
     if (kw == 1) {
-        switch (wq) {
-            case 1: return launch_one<D, BN, 1, 1>(p);
-            case 2: return launch_one<D, BN, 2, 1>(p);
-            case 4: return launch_one<D, BN, 4, 1>(p);
-            default: return hipErrorInvalidValue;
+        if constexpr (BN == 128) {
+            // 128-key tiles are built for 16-row query blocks only
+            if (wq == 1) return launch_one<D, BN, 1, 1>(p);
+            return hipErrorInvalidValue;
+        } else {
+            switch (wq) {
+                case 1: return launch_one<D, BN, 1, 1>(p);
+                case 2: return launch_one<D, BN, 2, 1>(p);
+                case 4: return launch_one<D, BN, 4, 1>(p);
+                default: return hipErrorInvalidValue;
+            }
         }
     }
     if (wq != 1) return hipErrorInvalidValue;
@@ -346,6 +352,9 @@ hipError_t by_waves(const Problem& p, int wq, int kw) {
     }
     if constexpr (BN >= 64) {
         if (kw == 4) return launch_one<D, BN, 1, 4>(p);
+    }
+    if constexpr (BN >= 128 && D < 128) {
+        if (kw == 8) return launch_one<D, BN, 1, 8>(p);
     }
     return hipErrorInvalidValue;
 }
@@ -356,6 +365,7 @@ hipError_t by_bn(const Problem& p, int bn, int wq, int kw) {
         case 16: return by_waves<D, 16>(p, wq, kw);
         case 32: return by_waves<D, 32>(p, wq, kw);
         case 64: return by_waves<D, 64>(p, wq, kw);
+        case 128: return by_waves<D, 128>(p, wq, kw);
         default: return hipErrorInvalidValue;
     }
 }
@@ -365,7 +375,8 @@ hipError_t by_bn(const Problem& p, int bn, int wq, int kw) {
 bool f32_tiles_supported(int d, int block_m, int block_n) {
     const bool dm = d == 16 || d == 32 || d == 64 || d == 128;
     const bool bm = block_m == 16 || block_m == 32 || block_m == 64;
-    const bool bn = block_n == 16 || block_n == 32 || block_n == 64;
+    const bool bn = block_n == 16 || block_n == 32 || block_n == 64 ||
+                    (block_n == 128 && block_m == 16);
     return dm && bm && bn;
 }
 
@@ -373,8 +384,11 @@ int f32_lds_bytes(int d, int /*block_m*/, int block_n) {
     return block_n * ((d + 4) + (d + 16)) * (int)sizeof(float);
 }
 
-int f32_key_waves(int block_m, int block_n, long query_tiles) {
+int f32_key_waves(int d, int block_m, int block_n, long query_tiles) {
     if (block_m != 16) return 1;
+    // 128-key tiles: eight waves of 16 keys each (four at d = 128, where
+    // eight would not fit two waves per SIMD in registers)
+    if (block_n == 128) return d == 128 ? 4 : 8;
     const int kw = query_tiles >= 1024 ? 1 : (query_tiles >= 512 ? 2 : 4);
     return kw < block_n / 16 ? kw : block_n / 16;
 }
@@ -383,7 +397,7 @@ hipError_t launch_f32(const Problem& p, const Tiles& t) {
     if (!f32_tiles_supported(p.d, t.block_m, t.block_n)) return hipErrorInvalidValue;
     const int wq = t.block_m / 16;
     const long n_qt = (p.Sq + t.block_m - 1) / t.block_m;
-    const int kw = f32_key_waves(t.block_m, t.block_n, (long)p.B * p.H * n_qt);
+    const int kw = f32_key_waves(p.d, t.block_m, t.block_n, (long)p.B * p.H * n_qt);
     switch (p.d) {
         case 16: return by_bn<16>(p, t.block_n, wq, kw);
         case 32: return by_bn<32>(p, t.block_n, wq, kw);

@@ -54,10 +54,11 @@ hipError_t launch_merge(const Problem& p);
 bool f32_tiles_supported(int d, int block_m, int block_n);
 bool bf16_tiles_supported(int d, int block_m, int block_n);
 int f32_lds_bytes(int d, int block_m, int block_n);
-// fp32 waves per 16-row query block (key groups of one workgroup): 4, 2 or 1
-// as the query-tile grid has fewer than 512, fewer than 1024 or more tiles,
-// at most block_n / 16, and 1 unless block_m = 16
-int f32_key_waves(int block_m, int block_n, long query_tiles);
+// fp32 waves per 16-row query block (key groups of one workgroup), 1 unless
+// block_m = 16: with 128-key tiles 8 (4 at d = 128); otherwise 4, 2 or 1 as
+// the query-tile grid has fewer than 512, fewer than 1024 or more tiles, at
+// most block_n / 16
+int f32_key_waves(int d, int block_m, int block_n, long query_tiles);
 int bf16_lds_bytes(int d, int block_m, int block_n);
 
 }  // namespace attn
