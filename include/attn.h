@@ -175,7 +175,8 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
  * n_splits = 0 (host only, no HIP call): 1 when the query tiles alone reach
  * the target, else enough chunks of whole key tiles to reach it (at most
  * 64).  Target: one workgroup per compute unit for 16-bit inputs, four
- * waves per compute unit (one per SIMD) for fp32.  Writes the count and the
+ * waves per compute unit (one per SIMD) for fp32; fp32 key ranges of fewer
+ * than four key tiles stay in one chunk.  Writes the count and the
  * chunk length in keys; either pointer may be NULL.  Returns as
  * attn_select_tiles.
  */

@@ -31,7 +31,7 @@ def test_split_stress_fp32(name, causal):
     q, k, v = make_tensors(w)
     auto, chunk = binding.select_splits(w.d, w.Sq, w.Skv, w.B * w.H, binding.F32, causal)
     log(f"{name} causal={causal}: library chooses {auto} chunks of {chunk} keys")
-    if w.Sq == 8 and w.Skv > 64:      # 64 keys are one tile: nothing to split
+    if w.Sq == 8 and w.Skv > 512:     # four or more 128-key tiles: split
         assert auto > 1
     for splits in (0, 2, 7):
         check_full(q, k, v, causal, splits=splits, what=f"{name} causal={causal} splits={splits}")
