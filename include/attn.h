@@ -120,8 +120,9 @@ int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* 
  * the chosen kernel decide its speed, so the choice is made here per head
  * dimension, dtype and grid size rather than fixed.  On the 16-bit path,
  * d = 32 takes 64-key tiles (a 32-key tile would give each step only two
- * score MFMAs, too few to hide the softmax under), d = 64 and 128 take
- * 32-key tiles.
+ * score MFMAs, too few to hide the softmax under), d = 64 takes 64-key
+ * tiles in 128-row workgroups and 32-key tiles in 64-row ones, d = 128
+ * takes 32-key tiles.
  * Writes the tile shape attn_fwd would use for this problem:
  * query rows per workgroup, key rows per tile, 64-wide waves per workgroup
  * and LDS bytes per workgroup.  fp32 waves own 16 query rows each; with

@@ -58,13 +58,14 @@ def test_version(lib):
     ((128, 4096, 4096, 32, B.BF16, 1), (128, 32, 4)),
     ((128, 32768, 32768, 64, B.BF16, 1), (128, 32, 4)),
     ((128, 256, 256, 2, B.BF16, 1), (64, 32, 2)),
-    ((64, 4096, 4096, 32, B.BF16_OUT_F32, 0), (128, 32, 4)),
+    ((64, 4096, 4096, 32, B.BF16_OUT_F32, 0), (128, 64, 4)),   # d = 64: 64-key tiles
+    ((64, 1024, 1024, 8, B.BF16, 1), (64, 32, 2)),              # ... but 32-key at 64 rows
     ((128, 4096, 4096, 16, B.BF16, 1), (128, 32, 4)),
     ((128, 1024, 1024, 2, B.BF16, 1), (64, 32, 2)),
     ((32, 4096, 4096, 32, B.BF16, 1), (128, 64, 4)),    # d = 32: 64-key tiles
     ((32, 512, 512, 2, B.F16, 0), (64, 64, 2)),
     ((128, 4096, 4096, 32, B.F16, 1), (128, 32, 4)),
-    ((64, 4096, 4096, 32, B.F16_OUT_F32, 0), (128, 32, 4)),
+    ((64, 4096, 4096, 32, B.F16_OUT_F32, 0), (128, 64, 4)),
 ])
 def test_selector(lib, args, want):
     bm, bn, waves, lds = B.select_tiles(*args)
