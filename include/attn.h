@@ -105,8 +105,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *                       (every d), and block_m = 16 with block_n = 128
  *   ATTN_BF16[_OUT_F32], ATTN_F16[_OUT_F32]
  *                       block_m in {64, 128},     block_n in {32, 64} (d = 64,
- *                       128) or block_n = 64 (d = 32), and block_m = 256
- *                       with block_n = 32 when d = 128
+ *                       128) or block_n = 64 (d = 32), block_m = 128 with
+ *                       block_n = 128 when d = 32, and block_m = 256 with
+ *                       block_n = 32 when d = 128
  * Any other pair returns ATTN_ERR_UNSUPPORTED.
  */
 int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -119,10 +120,10 @@ int attn_fwd_tiles(const void* q, const void* k, const void* v, void* o, float* 
  * runtime": the tile size, register pressure, cache reuse and precision of
  * the chosen kernel decide its speed, so the choice is made here per head
  * dimension, dtype and grid size rather than fixed.  On the 16-bit path,
- * d = 32 takes 64-key tiles (a 32-key tile would give each step only two
- * score MFMAs, too few to hide the softmax under), d = 64 takes 64-key
- * tiles in 128-row workgroups and 32-key tiles in 64-row ones, d = 128
- * takes 32-key tiles.
+ * d = 32 takes 128-key tiles in 128-row workgroups and 64-key tiles in
+ * 64-row ones (a 32-key tile would give each step only two score MFMAs, too
+ * few to hide the softmax under), d = 64 takes 64-key tiles in 128-row
+ * workgroups and 32-key tiles in 64-row ones, d = 128 takes 32-key tiles.
  * Writes the tile shape attn_fwd would use for this problem:
  * query rows per workgroup, key rows per tile, 64-wide waves per workgroup
  * and LDS bytes per workgroup.  fp32 waves own 16 query rows each; with

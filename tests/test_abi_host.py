@@ -62,7 +62,8 @@ def test_version(lib):
     ((64, 1024, 1024, 8, B.BF16, 1), (64, 32, 2)),              # ... but 32-key at 64 rows
     ((128, 4096, 4096, 16, B.BF16, 1), (128, 32, 4)),
     ((128, 1024, 1024, 2, B.BF16, 1), (64, 32, 2)),
-    ((32, 4096, 4096, 32, B.BF16, 1), (128, 64, 4)),    # d = 32: 64-key tiles
+    ((32, 4096, 4096, 32, B.BF16, 1), (128, 128, 4)),   # d = 32: 128-key tiles
+    ((32, 1024, 1024, 8, B.BF16, 1), (64, 64, 2)),      # ... 64-key at 64 rows
     ((32, 512, 512, 2, B.F16, 0), (64, 64, 2)),
     ((128, 4096, 4096, 32, B.F16, 1), (128, 32, 4)),
     ((64, 4096, 4096, 32, B.F16_OUT_F32, 0), (128, 64, 4)),
@@ -108,7 +109,7 @@ def _call(lib, q=A0, k=A1, v=A2, o=A3, lse=A4, Bn=1, H=2, Sq=64, Skv=64, d=64, s
     (dict(d=16, dtype=B.BF16), B.ERR_UNSUPPORTED),
     (dict(dtype=5), B.ERR_INVALID_ARG),
     (dict(d=16, dtype=B.F16), B.ERR_UNSUPPORTED),
-    (dict(d=32, dtype=B.BF16, tiles=(128, 32)), B.ERR_UNSUPPORTED),   # d = 32 takes 64-key tiles
+    (dict(d=32, dtype=B.BF16, tiles=(128, 32)), B.ERR_UNSUPPORTED),   # d = 32 takes 64- or 128-key tiles
     (dict(scale=float("nan")), B.ERR_INVALID_ARG),
     (dict(scale=float("inf")), B.ERR_INVALID_ARG),
     (dict(scale=0.0), B.ERR_INVALID_ARG),

@@ -174,13 +174,16 @@ def test_bf16_full_size_sampled(B_, H, Sq, Skv, d, causal, dist):
 # ------------------------------------------------------------------ smaller bf16 shapes, whole output
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("tiles", [(256, 32), (128, 64), (128, 32), (64, 64), (64, 32), None],
-                         ids=["256x32", "128x64", "128x32", "64x64", "64x32", "selector"])
+@pytest.mark.parametrize("tiles", [(256, 32), (128, 128), (128, 64), (128, 32), (64, 64), (64, 32),
+                                   None],
+                         ids=["256x32", "128x128", "128x64", "128x32", "64x64", "64x32", "selector"])
 def test_bf16_ragged_tiles(d, causal, tiles):
     if tiles == (256, 32) and d != 128:
         pytest.skip("256-row tiles are built for d = 128 only")
-    if d == 32 and tiles is not None and tiles[1] != 64:
-        pytest.skip("d = 32 takes 64-key tiles only")
+    if tiles == (128, 128) and d != 32:
+        pytest.skip("128-key tiles are built for d = 32 only")
+    if d == 32 and tiles is not None and tiles[1] == 32:
+        pytest.skip("d = 32 takes 64- or 128-key tiles only")
     q, k, v = random_tensors(1, 3, 300, 333, d, "bf16", "uniform0.8", seed=17 + d)
     log(f"bf16 ragged d={d} causal={causal} tiles={tiles}")
     check_full(q, k, v, causal, tiles=tiles, what=f"bf16 300x333 d={d}")
@@ -189,8 +192,10 @@ def test_bf16_ragged_tiles(d, causal, tiles):
 
 
 @pytest.mark.parametrize("d,tiles", [(128, (128, 32)), (128, (64, 64)), (128, (256, 32)),
-                                     (32, (128, 64)), (32, (64, 64))],
-                         ids=["d128-128x32", "d128-64x64", "d128-256x32", "d32-128x64", "d32-64x64"])
+                                     (64, (128, 64)), (32, (128, 128)), (32, (128, 64)),
+                                     (32, (64, 64))],
+                         ids=["d128-128x32", "d128-64x64", "d128-256x32", "d64-128x64",
+                              "d32-128x128", "d32-128x64", "d32-64x64"])
 def test_bf16_every_tile_count(d, tiles):
     # key lengths giving 1 .. 10 key tiles, full and ragged, so that every
     # entry and exit of the pipelined tile loop runs: no next tile, the

@@ -27,7 +27,7 @@ TILES = {"f32": {16: [(16, 16), (32, 64), (64, 32), (16, 64), (16, 128)],
                  32: [(16, 64), (64, 16), (32, 32), (16, 128)],
                  64: [(32, 32), (64, 64), (16, 64), (16, 128)],
                  128: [(16, 32), (64, 64), (16, 128)]},
-         "bf16": {32: [(128, 64), (64, 64)], 64: [(128, 32), (64, 64), (64, 32), (128, 64)],
+         "bf16": {32: [(128, 64), (64, 64), (128, 128)], 64: [(128, 32), (64, 64), (64, 32), (128, 64)],
                   128: [(256, 32), (128, 64), (64, 32), (128, 32), (64, 64)]}}
 TILES["f16"] = TILES["bf16"]
 CODE = {("f32", False): binding.F32, ("bf16", False): binding.BF16,

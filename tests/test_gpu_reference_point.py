@@ -139,7 +139,7 @@ def one_rise(d, delta, jump, dtype, Sq=96, Skv=300, H=2, seed=77):
 def test_rise_at_fp16_limit(delta, dtype, tiles):
     for d in (32, 64, 128):
         if d == 32 and tiles == (64, 32):
-            continue   # d = 32 takes 64-key tiles only
+            continue   # d = 32 takes 64- or 128-key tiles only
         q, k, v, scale = one_rise(d, delta, jump=150, dtype=dtype)
         for causal in (False, True):
             log(f"one rise of {delta} (base 2) d={d} {dtype} causal={causal} tiles={tiles}")

@@ -717,7 +717,9 @@ hipError_t launch_one(const Problem& p) {
 template <typename T, int D, bool OUT_F32>
 hipError_t by_tiles(const Problem& p, int bm, int bn) {
     if constexpr (D == 32) {
-        // a 32-key tile holds only two score MFMAs at d = 32: 64-key tiles
+        // a 32-key tile holds only two score MFMAs at d = 32: 64- or 128-key
+        // tiles
+        if (bm == 128 && bn == 128) return launch_one<T, D, 128, 4, OUT_F32>(p);
         if (bm == 128 && bn == 64) return launch_one<T, D, 64, 4, OUT_F32>(p);
         if (bm == 64 && bn == 64) return launch_one<T, D, 64, 2, OUT_F32>(p);
     } else {
@@ -736,7 +738,9 @@ hipError_t by_tiles(const Problem& p, int bm, int bn) {
 
 bool bf16_tiles_supported(int d, int block_m, int block_n) {
     if (!(d == 32 || d == 64 || d == 128)) return false;
-    if (d == 32) return (block_m == 64 || block_m == 128) && block_n == 64;
+    if (d == 32)
+        return ((block_m == 64 || block_m == 128) && block_n == 64) ||
+               (block_m == 128 && block_n == 128);
     if (block_m == 256) return d == 128 && block_n == 32;
     return (block_m == 64 || block_m == 128) && (block_n == 32 || block_n == 64);
 }
