@@ -33,7 +33,8 @@ def test_single_head_s64_d32(causal, tiles):
     check_full(q, k, v, causal, tiles=tiles, what="single_head_s64_d32")
 
 
-@pytest.mark.parametrize("tiles", [(64, 64), None], ids=["tiles64", "selector"])
+@pytest.mark.parametrize("tiles", [(16, 64), (64, 64), None],
+                         ids=["tiles16x64", "tiles64x64", "selector"])
 def test_b2h4_s512_d64(tiles):
     w = WORKLOADS["b2h4_s512_d64"]
     q, k, v = make_tensors(w)
