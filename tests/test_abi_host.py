@@ -296,3 +296,31 @@ def test_probe_library_exports_its_header_and_rejects_bad_kinds():
     assert probe.attn_probe_mfma(0, 0, 4, 0x1000, None) == 1
     assert probe.attn_probe_mfma(0, 10, 4, None, None) == 1
     assert probe.attn_probe_mfma_flops(1, 10, 4) == 16 * 2 * 32 * 32 * 16 * 10 * 4 * 4
+
+
+def test_last_error_is_per_thread(lib):
+    # a failing call on one thread keeps its message while another thread's
+    # calls succeed (and clear only their own message)
+    import threading
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def failing():
+        st = lib.attn_select_tiles(48, 64, 64, 1, B.F32, 0, None, None, None, None)
+        barrier.wait()          # the other thread succeeds in between
+        barrier.wait()
+        seen["fail"] = (st, lib.attn_last_error().decode())
+
+    def succeeding():
+        barrier.wait()
+        st = lib.attn_select_tiles(64, 64, 64, 1, B.F32, 0, None, None, None, None)
+        seen["ok"] = (st, lib.attn_last_error().decode())
+        barrier.wait()
+
+    threads = [threading.Thread(target=failing), threading.Thread(target=succeeding)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=30)
+    assert seen["fail"][0] == B.ERR_UNSUPPORTED and "48" in seen["fail"][1]
+    assert seen["ok"] == (B.OK, "")
