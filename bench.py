@@ -335,6 +335,10 @@ def main(argv=None) -> int:
     ap.add_argument("--mfma-probe", type=int, default=0, metavar="ITERS",
                     help="time bare bf16 MFMA streams (zero / random operands, with and "
                          "without LDS operand reads) from libattn_probe.so")
+    ap.add_argument("--launch-series", type=int, default=0, metavar="N",
+                    help="diagnostic: N launches from a cold start (no warm-up), each "
+                         "between its own event pair, printed as one JSON line of "
+                         "per-launch times (the GPU's clock ramp)")
     ap.add_argument("--flush", action="store_true",
                     help="overwrite a 1 GiB buffer before each timed launch (outside the "
                          "per-launch events), so K/V start outside L2 and Infinity Cache; "
@@ -417,6 +421,28 @@ def main(argv=None) -> int:
             binding.fwd_split_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   lse.data_ptr(), w.B, w.H, w.Sq, w.Skv, w.d, scale, causal, code,
                                   sp, n_splits, ws.data_ptr(), ws_bytes)
+
+    if a.launch_series:
+        # back to back on the launch stream, one event pair per launch
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(a.launch_series)]
+        torch.cuda.synchronize()
+        for s0, s1 in pairs:
+            s0.record(stream)
+            step()
+            s1.record(stream)
+        torch.cuda.synchronize()
+        us = [round(s0.elapsed_time(s1) * 1e3, 2) for s0, s1 in pairs]
+
+        def mean(lo, hi):
+            part = us[lo:hi]
+            return round(sum(part) / len(part), 2) if part else None
+        print(json.dumps({"launch_series": a.launch_series, "workload": a.workload,
+                          "us_mean": {"1-5": mean(0, 5), "6-25": mean(5, 25),
+                                      "26-100": mean(25, 100), "101-300": mean(100, 300),
+                                      "last 100": mean(len(us) - 100, len(us))},
+                          "us": us}), flush=True)
+        return 0
 
     for _ in range(a.warmup):
         step()
