@@ -57,3 +57,12 @@ def test_mfma_probe_line():
         r = rec[name]
         assert 0 < r["frac_of_peak"] <= 1.0, (name, r)
     assert rec["mfma_zero"]["tflops"] >= 0.9 * rec["mfma_random"]["tflops"]
+
+
+def test_launch_series_line():
+    # the cold-start series: one positive time per launch, window means that
+    # agree with the times
+    rec = run_bench("--launch-series", "12", "--workload", "single_head_s64_d32")
+    us = rec["us"]
+    assert rec["launch_series"] == 12 and len(us) == 12 and all(t > 0 for t in us)
+    assert rec["us_mean"]["6-25"] == round(sum(us[5:]) / len(us[5:]), 2)
